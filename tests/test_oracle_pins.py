@@ -1,0 +1,377 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU needed).
+
+Each test checks one oracle function against something other than its own formula: brute
+force on tiny inputs, an independent library routine, a closed form, an invariant of the
+method, or a hand-derived case under tests/golden/.  A plausible mistake in the oracle (a
+dropped term, a wrong sign, index or bit order, a transposed operand) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------------------------------------
+# routing
+# ------------------------------------------------------------------------------------------
+def _bruteforce_route(logits, k):
+    """Rank of e = #experts strictly larger + #equal experts with a lower id."""
+    T, E = logits.shape
+    ids = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        row = [float(v) for v in logits[t]]
+        for e in range(E):
+            rank = sum(1 for f in range(E) if row[f] > row[e] or (row[f] == row[e] and f < e))
+            if rank < k:
+                ids[t, rank] = e
+    return ids
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (13, 5), (16, 16), (5, 1)])
+def test_route_ids_match_bruteforce_rank(E, k):
+    r = _rng(E * 100 + k)
+    # fp16-grid values create many exact ties
+    logits = (r.standard_normal((9, E)) * 2).astype(np.float16).astype(np.float32)
+    logits[0, :] = 0.5                     # a fully tied row
+    logits[1, ::2] = -0.0
+    logits[1, 1::2] = 0.0                  # signed zeros
+    ids, gates = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(ids, _bruteforce_route(logits, k))
+
+
+def test_route_first_choice_is_numpy_argmax():
+    r = _rng(1)
+    logits = r.integers(-3, 4, size=(64, 17)).astype(np.float32)  # heavy ties
+    ids, _ = oracle.route_topk(logits, 4)
+    np.testing.assert_array_equal(ids[:, 0], np.argmax(logits, axis=1))  # first max = lowest id
+
+
+def test_route_exactly_k_distinct_in_range_and_k_equals_E_is_full_order():
+    r = _rng(2)
+    logits = r.standard_normal((20, 11)).astype(np.float32)
+    for k in (1, 3, 11):
+        ids, gates = oracle.route_topk(logits, k)
+        assert ids.shape == (20, k)
+        for t in range(20):
+            assert len(set(ids[t].tolist())) == k
+            assert ids[t].min() >= 0 and ids[t].max() < 11
+    ids, _ = oracle.route_topk(logits, 11)
+    np.testing.assert_array_equal(ids, np.argsort(-logits.astype(np.float64), axis=1, kind="stable"))
+
+
+def test_route_gates_equal_full_softmax_renormalised():
+    r = _rng(3)
+    logits = (r.standard_normal((30, 40)) * 3).astype(np.float32)
+    k = 7
+    ids, gates = oracle.route_topk(logits, k)
+    l = logits.astype(np.float64)
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)                       # full-E softmax
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(gates, sel / sel.sum(axis=1, keepdims=True), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(gates.sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(np.diff(gates, axis=1) <= 1e-15)         # non-increasing along the slots
+
+
+def test_route_golden_cases():
+    with open(os.path.join(GOLDEN, "routing_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        logits = np.array([[float(v) for v in c["logits"]]], dtype=np.float32)
+        ids, gates = oracle.route_topk(logits, c["k"])
+        assert ids[0].tolist() == c["ids"], c["note"]
+        np.testing.assert_allclose(gates[0], c["gates"], rtol=0, atol=c["tol"] + 1e-16,
+                                   err_msg=c["note"])
+
+
+def test_route_rejects_non_finite_and_bad_k():
+    with pytest.raises(ValueError):
+        oracle.route_topk(np.array([[0.0, np.nan]], dtype=np.float32), 1)
+    with pytest.raises(ValueError):
+        oracle.route_topk(np.zeros((1, 3), dtype=np.float32), 4)
+
+
+def test_route_empty_batch():
+    ids, gates = oracle.route_topk(np.zeros((0, 6), dtype=np.float32), 2)
+    assert ids.shape == (0, 2) and gates.shape == (0, 2)
+
+
+# ------------------------------------------------------------------------------------------
+# grouping
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(4, 8, 2), (33, 16, 5), (1, 3, 3), (50, 64, 8)])
+def test_group_matches_stable_argsort_and_inverts(T, E, k):
+    r = _rng(T * E + k)
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    logits[:, 0] += 3.0                              # a hot expert
+    ids, _ = oracle.route_topk(logits, k)
+    offsets, pairs, active, n_active = oracle.group_by_expert(ids, E)
+    flat = ids.reshape(-1)
+    np.testing.assert_array_equal(pairs, np.argsort(flat, kind="stable"))
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+    assert offsets[-1] == T * k
+    assert sorted(pairs.tolist()) == list(range(T * k))            # bijection
+    rebuilt = np.empty(T * k, dtype=np.int64)
+    for e in range(E):
+        rebuilt[pairs[offsets[e]:offsets[e + 1]]] = e
+    np.testing.assert_array_equal(rebuilt, flat)
+    uniq = np.unique(flat)
+    assert n_active == len(uniq)
+    np.testing.assert_array_equal(active[:n_active], uniq)
+    assert np.all(active[n_active:] == -1)
+
+
+def test_group_empty():
+    offsets, pairs, active, n_active = oracle.group_by_expert(np.zeros((0, 2), dtype=np.int32), 5)
+    assert n_active == 0 and len(pairs) == 0 and np.all(offsets == 0)
+
+
+# ------------------------------------------------------------------------------------------
+# bit-plane format
+# ------------------------------------------------------------------------------------------
+def test_bit_position_is_a_bijection_per_plane():
+    for p in range(8):
+        pos = oracle.bit_position(p, np.arange(32))
+        assert sorted(pos.tolist()) == list(range(32))
+
+
+@pytest.mark.parametrize("q", range(1, 9))
+def test_pack_unpack_round_trip_gives_top_q_bit_prefix(q):
+    r = _rng(q)
+    idx8 = r.integers(0, 256, size=(128, 384), dtype=np.uint8)
+    planes = oracle.pack_planes(idx8, q)
+    assert planes.dtype == np.uint32 and planes.size == q * 128 * 384 // 32
+    got = oracle.unpack_planes(planes, 128, 384, q)
+    np.testing.assert_array_equal(got, idx8 >> (8 - q))
+    np.testing.assert_array_equal(oracle.committed_index(idx8, q), idx8 >> (8 - q))
+
+
+def test_dropping_tail_planes_equals_repacking_at_lower_width():
+    r = _rng(11)
+    idx8 = r.integers(0, 256, size=(64, 256), dtype=np.uint8)
+    full = oracle.pack_planes(idx8, 8)
+    per_plane = 64 * 256 // 32
+    for q in range(1, 8):
+        np.testing.assert_array_equal(full[: q * per_plane], oracle.pack_planes(idx8, q))
+
+
+def test_plane_p_holds_bit_7_minus_p_row_by_row():
+    """Popcount of plane p, per row, equals the count of parent indices with bit 7-p set."""
+    r = _rng(12)
+    R, C = 128, 256
+    idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
+    planes = oracle.pack_planes(idx8, 8).reshape(8, -1)
+    for p in range(8):
+        total = int(np.unpackbits(planes[p].view(np.uint8)).sum())
+        assert total == int(((idx8 >> (7 - p)) & 1).sum())
+    # a single full-scale index lights exactly one bit in every plane, none elsewhere
+    one = np.zeros((R, C), dtype=np.uint8)
+    one[70, 201] = 0xFF
+    pl = oracle.pack_planes(one, 8).reshape(8, -1)
+    loc = [np.flatnonzero(pl[p]) for p in range(8)]
+    assert all(len(l) == 1 for l in loc)
+    assert len({int(l[0]) for l in loc}) == 1          # same word offset in every plane
+    bits = [int(pl[p][loc[p][0]]) for p in range(8)]
+    assert all(b and (b & (b - 1)) == 0 for b in bits)  # one bit each
+    # all-0x80 -> plane 0 all ones, other planes empty
+    msb = np.full((R, C), 0x80, dtype=np.uint8)
+    pl = oracle.pack_planes(msb, 3).reshape(3, -1)
+    assert np.all(pl[0] == 0xFFFFFFFF) and not pl[1:].any()
+
+
+def test_format_rejects_bad_shapes():
+    with pytest.raises(ValueError):
+        oracle.pack_planes(np.zeros((64, 96), dtype=np.uint8), 4)
+    with pytest.raises(ValueError):
+        oracle.pack_planes(np.zeros((32, 128), dtype=np.uint8), 4)
+
+
+# ------------------------------------------------------------------------------------------
+# dequantised GEMV
+# ------------------------------------------------------------------------------------------
+def _naive_matvec(idx_q, lut, X):
+    R, C = idx_q.shape
+    n = X.shape[1]
+    Y = np.zeros((R, n))
+    for r in range(R):
+        for c in range(C):
+            w = float(lut[r, idx_q[r, c]])
+            for j in range(n):
+                Y[r, j] += w * float(X[c, j])
+    return Y
+
+
+def test_apq_matvec_matches_naive_loops():
+    r = _rng(20)
+    q = 3
+    idx8 = r.integers(0, 256, size=(64, 128), dtype=np.uint8)
+    lut = (r.standard_normal((64, 1 << q)) * 0.02).astype(np.float16)
+    X = r.standard_normal((128, 3))
+    idx_q = oracle.committed_index(idx8, q)
+    Y = oracle.apq_matvec(idx_q, lut, X)
+    np.testing.assert_allclose(Y, _naive_matvec(idx_q, lut, X), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.apq_matvec(idx_q, lut, X, row_chunk=7), Y, rtol=1e-13, atol=1e-15)
+
+
+def test_apq_matvec_closed_forms():
+    r = _rng(21)
+    R, C, q = 64, 256, 5
+    idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
+    idx_q = oracle.committed_index(idx8, q)
+    X = r.integers(-4, 5, size=(C, 2)).astype(np.float64)          # integers: exact sums
+    # constant LUT row: y_r = a * sum(x)
+    a = np.float16(0.375)
+    lut = np.full((R, 1 << q), a, dtype=np.float16)
+    np.testing.assert_array_equal(oracle.apq_matvec(idx_q, lut, X), np.broadcast_to(float(a) * X.sum(0), (R, 2)))
+    # affine LUT lut[v] = a + b v (fp16-exact): y_r = a sum(x) + b sum(idx x)
+    b = np.float16(0.125)
+    lut = (float(a) + float(b) * np.arange(1 << q))[None, :].repeat(R, 0).astype(np.float16)
+    expect = float(a) * X.sum(0)[None, :] + float(b) * (idx_q.astype(np.float64) @ X)
+    np.testing.assert_array_equal(oracle.apq_matvec(idx_q, lut, X), expect)
+
+
+def test_one_hot_probe_reads_the_lut_entry():
+    r = _rng(22)
+    R, C, q = 64, 128, 6
+    idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
+    lut = (r.standard_normal((R, 1 << q))).astype(np.float16)
+    idx_q = oracle.committed_index(idx8, q)
+    for c in (0, 37, 127):
+        X = np.zeros((C, 1))
+        X[c] = 1.0
+        y = oracle.apq_matvec(idx_q, lut, X)[:, 0]
+        np.testing.assert_array_equal(y, lut[np.arange(R), idx_q[:, c]].astype(np.float64))
+
+
+def test_silu_identities():
+    z = np.linspace(-30, 30, 1001)
+    s = oracle.silu(z)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(s - oracle.silu(-z), z, atol=1e-12)
+    np.testing.assert_allclose(s, z * expit(z), rtol=1e-13, atol=1e-300)
+
+
+# ------------------------------------------------------------------------------------------
+# the layer
+# ------------------------------------------------------------------------------------------
+def _tiny_layer(shape, seed=0):
+    inputs = wl.gen_layer_inputs(shape, seed)
+    blocks = {}
+
+    def get(e, m):
+        if (e, m) not in blocks:
+            b = wl.gen_block(shape, e, m, int(inputs.widths[e, m]))
+            blocks[(e, m)] = (b.idx8, b.q, b.lut)
+        return blocks[(e, m)]
+    return inputs, get
+
+
+def _dense_W(idx8, q, lut):
+    R, C = idx8.shape
+    W = np.zeros((R, C))
+    for r in range(R):
+        W[r] = [float(lut[r, v >> (8 - q)]) for v in idx8[r]]
+    return W
+
+
+def test_layer_equals_dense_bruteforce_over_all_experts():
+    """Every expert on every token, weighted by a dense gate matrix (no grouping logic)."""
+    shape = wl.TINY.replace(T=6)
+    inputs, get = _tiny_layer(shape)
+    res = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get)
+    T, E, H, I = shape.T, shape.E, shape.H, shape.I
+    G = np.zeros((T, E))
+    l = inputs.logits.astype(np.float64)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-l[t, e], e))[: shape.k]
+        w = np.array([math.exp(l[t, e] - l[t, order[0]]) for e in order])
+        G[t, order] = w / w.sum()
+    y = np.zeros((T, H))
+    x = inputs.x.astype(np.float64)
+    for e in range(E):
+        Wgu = _dense_W(*get(e, 0))
+        Wd = _dense_W(*get(e, 1))
+        h = x @ Wgu.T
+        act = h[:, :I] * expit(h[:, :I]) * h[:, I:]
+        y += G[:, e:e + 1] * (act @ Wd.T)
+    np.testing.assert_allclose(res["y"], y, rtol=1e-10, atol=1e-12)
+
+
+def test_identical_experts_make_output_routing_invariant():
+    shape = wl.TINY.replace(T=5, E=6, k=3)
+    inputs, get = _tiny_layer(shape)
+    fixed = {m: get(0, m) for m in (0, 1)}
+    same = lambda e, m: fixed[m]
+    y1 = oracle.layer_forward(inputs.x, inputs.logits, 3, same)["y"]
+    r = _rng(5)
+    y2 = oracle.layer_forward(inputs.x, r.standard_normal(inputs.logits.shape).astype(np.float32), 3, same)["y"]
+    ffn = oracle.expert_ffn(oracle.committed_index(fixed[0][0], fixed[0][1]), fixed[0][2],
+                            oracle.committed_index(fixed[1][0], fixed[1][1]), fixed[1][2], inputs.x)
+    np.testing.assert_allclose(y1, ffn, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(y2, ffn, rtol=1e-12, atol=1e-14)
+
+
+def test_k1_output_is_the_first_choice_ffn_and_shared_adds_linearly():
+    shape = wl.TINY.replace(T=4, k=1)
+    inputs, get = _tiny_layer(shape)
+    res = oracle.layer_forward(inputs.x, inputs.logits, 1, get)
+    for t in range(shape.T):
+        e = int(res["ids"][t, 0])
+        gi, gq, gl = get(e, 0)
+        di, dq, dl = get(e, 1)
+        yt = oracle.expert_ffn(oracle.committed_index(gi, gq), gl, oracle.committed_index(di, dq), dl,
+                               inputs.x[t:t + 1])
+        np.testing.assert_allclose(res["y"][t], yt[0], rtol=1e-12, atol=1e-14)
+    # a shared expert adds s_t * FFN_shared(x_t); scale 0 removes it, scale 2 doubles it
+    sh = lambda e, m: get(3, m)
+    base = res["y"]
+    ffn_sh = oracle.layer_forward(inputs.x, inputs.logits, 1, get, shared=sh)["y"] - base
+    s = np.array([0.0, 1.0, 2.0, -0.5])
+    y_s = oracle.layer_forward(inputs.x, inputs.logits, 1, get, shared=sh, shared_scale=s)["y"]
+    np.testing.assert_allclose(y_s - base, s[:, None] * ffn_sh, rtol=1e-10, atol=1e-13)
+
+
+def test_token_subset_matches_full_rows():
+    shape = wl.TINY.replace(T=7)
+    inputs, get = _tiny_layer(shape, seed=3)
+    full = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get)["y"]
+    part = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, tokens=[1, 5])["y"]
+    np.testing.assert_allclose(part[[1, 5]], full[[1, 5]], rtol=1e-12, atol=1e-16)
+    assert not part[[0, 2, 3, 4, 6]].any()
+
+
+def test_rel_l2():
+    a = np.array([3.0, 4.0])
+    assert oracle.rel_l2(a, a) == 0.0
+    assert abs(oracle.rel_l2(a * 1.001, a) - 1e-3) < 1e-12
+
+
+# ------------------------------------------------------------------------------------------
+# the seeded generators (determinism and the stated distributions)
+# ------------------------------------------------------------------------------------------
+def test_generators_are_deterministic_and_luts_nested():
+    shape = wl.TINY
+    a = wl.gen_block(shape, 3, 1)
+    b = wl.gen_block(shape, 3, 1)
+    np.testing.assert_array_equal(a.idx8, b.idx8)
+    np.testing.assert_array_equal(a.lut, b.lut)
+    assert a.q in shape.widths and a.lut.shape == (shape.H, 1 << a.q)
+    assert np.all(np.diff(a.lut.astype(np.float64), axis=1) >= 0)           # sorted rows
+    l3 = wl.gen_lut(shape, 3, 1, 3).astype(np.float64)
+    l4 = wl.gen_lut(shape, 3, 1, 4).astype(np.float64)
+    np.testing.assert_allclose(l3, l4.reshape(-1, 8, 2).mean(2), atol=4e-5)  # nested prefixes
+    w = wl.gen_widths(wl.QWEN3_NEXT_80B_A3B)
+    assert (w[:, 0] == 8).sum() >= 128 and set(np.unique(w).tolist()) <= {3, 4, 5, 6, 8}
+    assert np.all(wl.gen_widths(wl.QWEN15_MOE_A27B) == 4)
