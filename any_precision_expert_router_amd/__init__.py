@@ -1,0 +1,260 @@
+"""Thin Python binding of libmoe_apq (the MI355X decode-time Any-Precision MoE layer).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels behind the C ABI
+declared in ``include/moe_apq.h``.  PyTorch provides device memory and the stream; the
+functions here take torch tensors, pass their device pointers and the current stream, and
+raise :class:`MoeError` on a non-zero return code.  There is no CPU fallback: importing this
+module fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_apq.so")
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EWORKSPACE = -3
+MOE_EHIP = -4
+MOE_EDEVICE = -5
+MOE_PAGE_GPU, MOE_PAGE_CPU, MOE_PAGE_IN_TRANSFER = 0, 1, 2
+GATE_UP, DOWN = 0, 1
+
+EXPORTED = (
+    "moe_route_topk", "moe_group_by_expert", "moe_apq_ffn", "moe_layer_forward",
+    "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
+    "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_last_error",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} returned {code}: {msg}")
+        self.code = code
+
+
+class ApqBlock(ctypes.Structure):
+    """One weight-page-table entry (``moe_apq_block``, 32 bytes)."""
+
+    _fields_ = [
+        ("planes", ctypes.c_void_p),
+        ("lut", ctypes.c_void_p),
+        ("rows", ctypes.c_int32),
+        ("cols", ctypes.c_int32),
+        ("q", ctypes.c_uint8),
+        ("desired", ctypes.c_uint8),
+        ("state", ctypes.c_uint8),
+        ("reserved0", ctypes.c_uint8),
+        ("reserved1", ctypes.c_int32),
+    ]
+
+
+assert ctypes.sizeof(ApqBlock) == 32
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    sig = {
+        "moe_route_topk": ([P, I, I, I, P, P, S], I),
+        "moe_group_by_expert": ([P, I, I, I, P, P, P, P, P, Z, S], I),
+        "moe_apq_ffn": ([P, I, I, I, P, I, I, P, P, P, P, P, P, I, P, I, P, P, Z, S], I),
+        "moe_layer_forward": ([P, P, I, I, I, I, I, P, P, I, P, I, P, P, Z, S], I),
+        "moe_workspace_bytes": ([I, I, I, I, I, I], Z),
+        "moe_apq_pack": ([P, I, I, I, P], I),
+        "moe_apq_gemv": ([P, P, I, P, S], I),
+        "moe_apq_decode_indices": ([P, P, S], I),
+        "moe_check_device_error": ([P, Z, S], I),
+        "moe_profile_start": ([], I),
+        "moe_profile_stop": ([I, P, P, P], I),
+        "moe_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(fn, rc, _lib.moe_last_error().decode(errors="replace"))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ---------------------------------------------------------------------------------------------
+# The four entry points of the layer (same names as the C ABI)
+# ---------------------------------------------------------------------------------------------
+def moe_route_topk(logits, k: int, topk_ids, topk_gates, stream=None) -> None:
+    """logits fp32 [T, E] -> topk_ids int32 [T, k], topk_gates fp32 [T, k] (device tensors)."""
+    T, E = logits.shape
+    _check("moe_route_topk", _lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_ids),
+                                                 _ptr(topk_gates), _stream(stream)))
+
+
+def moe_group_by_expert(topk_ids, E: int, expert_offsets, sorted_pairs, active_experts, n_active,
+                        stream=None) -> None:
+    T, k = topk_ids.shape
+    _check("moe_group_by_expert", _lib.moe_group_by_expert(
+        _ptr(topk_ids), T, k, E, _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(active_experts),
+        _ptr(n_active), None, 0, _stream(stream)))
+
+
+def moe_apq_ffn(table, E: int, H: int, I: int, x, k: int, expert_offsets, sorted_pairs,
+                active_experts, n_active, topk_gates, y, workspace, shared=None, I_shared: int = 0,
+                shared_scale=None, prefill_threshold: int = 0, stream=None) -> None:
+    T = x.shape[0]
+    _check("moe_apq_ffn", _lib.moe_apq_ffn(
+        _ptr(table), E, H, I, _ptr(x), T, k, _ptr(expert_offsets), _ptr(sorted_pairs),
+        _ptr(active_experts), _ptr(n_active), _ptr(topk_gates), _ptr(shared), I_shared,
+        _ptr(shared_scale), prefill_threshold, _ptr(y), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+
+
+def moe_layer_forward(logits, x, E: int, H: int, I: int, k: int, table, y, workspace, shared=None,
+                      I_shared: int = 0, shared_scale=None, prefill_threshold: int = 0,
+                      stream=None) -> None:
+    T = x.shape[0]
+    _check("moe_layer_forward", _lib.moe_layer_forward(
+        _ptr(logits), _ptr(x), T, E, H, I, k, _ptr(table), _ptr(shared), I_shared,
+        _ptr(shared_scale), prefill_threshold, _ptr(y), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+
+
+def moe_workspace_bytes(T: int, E: int, H: int, I: int, k: int, I_shared: int = 0) -> int:
+    n = _lib.moe_workspace_bytes(T, E, H, I, k, I_shared)
+    if n == 0:
+        raise MoeError("moe_workspace_bytes", MOE_EINVAL, "bad sizes")
+    return n
+
+
+def moe_apq_pack(idx8: np.ndarray, q: int) -> np.ndarray:
+    """Host packer: uint8 [rows, cols] parent indices -> uint32 planes [q * rows * cols / 32]."""
+    idx8 = np.ascontiguousarray(idx8, dtype=np.uint8)
+    rows, cols = idx8.shape
+    out = np.empty(q * rows * cols // 32, dtype=np.uint32)
+    _check("moe_apq_pack", _lib.moe_apq_pack(idx8.ctypes.data, rows, cols, q, out.ctypes.data))
+    return out
+
+
+def moe_apq_gemv(block: ApqBlock, x, y, stream=None) -> None:
+    """Decode GEMV on one block: x fp16 [T, cols] -> y fp32 [T, rows]."""
+    _check("moe_apq_gemv", _lib.moe_apq_gemv(ctypes.byref(block), _ptr(x), x.shape[0], _ptr(y),
+                                             _stream(stream)))
+
+
+def moe_apq_decode_indices(block: ApqBlock, idx_out, stream=None) -> None:
+    _check("moe_apq_decode_indices", _lib.moe_apq_decode_indices(ctypes.byref(block), _ptr(idx_out),
+                                                                 _stream(stream)))
+
+
+def moe_check_device_error(workspace, stream=None) -> None:
+    _check("moe_check_device_error", _lib.moe_check_device_error(_ptr(workspace), workspace.numel(),
+                                                                 _stream(stream)))
+
+
+def moe_profile_start() -> None:
+    _check("moe_profile_start", _lib.moe_profile_start())
+
+
+def moe_profile_stop(max_kernels: int = 32) -> dict:
+    """{kernel name: (total ms, launches)} for the launches since moe_profile_start()."""
+    names = ctypes.create_string_buffer(64 * max_kernels)
+    ms = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int32 * max_kernels)()
+    n = _lib.moe_profile_stop(max_kernels, names, ms, cnt)
+    if n < 0:
+        _check("moe_profile_stop", n)
+    raw = names.raw
+    out = {}
+    for i in range(min(n, max_kernels)):
+        name = raw[64 * i: 64 * i + 64].split(b"\0", 1)[0].decode()
+        out[name] = (ms[i], cnt[i])
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# Device-resident weights: planes + LUTs per block and the weight page table
+# ---------------------------------------------------------------------------------------------
+class DeviceLayer:
+    """Device copies of a layer's blocks and its page table ([E][2] descriptors).
+
+    Blocks are packed on the host by ``moe_apq_pack`` and copied into one device arena per
+    layer (16-byte aligned sub-buffers).  ``table`` is the device page table consumed by
+    ``moe_apq_ffn``/``moe_layer_forward``; ``shared`` the optional shared-expert pair.
+    """
+
+    def __init__(self, E: int, H: int, I: int, blocks, shared_blocks=None, I_shared: int = 0,
+                 device="cuda"):
+        import torch
+        self.E, self.H, self.I, self.I_shared = E, H, I, I_shared if shared_blocks else 0
+        entries = []   # (planes ndarray uint32, lut ndarray fp16, rows, cols, q)
+        for e in range(E):
+            for m in (GATE_UP, DOWN):
+                entries.append(blocks(e, m))
+        sh_entries = [shared_blocks(m) for m in (GATE_UP, DOWN)] if shared_blocks else []
+        all_entries = entries + sh_entries
+        # one arena: planes and LUTs at 256-byte aligned offsets
+        offs, total = [], 0
+        for planes, lut, *_ in all_entries:
+            po = total
+            total += (planes.nbytes + 255) // 256 * 256
+            lo = total
+            total += (lut.nbytes + 255) // 256 * 256
+            offs.append((po, lo))
+        host = np.zeros(total, dtype=np.uint8)
+        for (po, lo), (planes, lut, *_) in zip(offs, all_entries):
+            host[po:po + planes.nbytes] = planes.view(np.uint8)
+            host[lo:lo + lut.nbytes] = np.ascontiguousarray(lut).view(np.uint8).reshape(-1)
+        self.arena = torch.from_numpy(host).to(device)
+        base = self.arena.data_ptr()
+        descs = []
+        for (po, lo), (planes, lut, rows, cols, q) in zip(offs, all_entries):
+            descs.append(ApqBlock(base + po, base + lo, rows, cols, q, q, MOE_PAGE_GPU, 0, 0))
+        self.host_blocks = descs
+        raw = np.frombuffer(b"".join(bytes(d) for d in descs), dtype=np.uint8)
+        self.table = torch.from_numpy(raw[: 32 * 2 * E].copy()).to(device)
+        self.shared = torch.from_numpy(raw[32 * 2 * E:].copy()).to(device) if sh_entries else None
+        self.weight_bytes = int(total)
+
+    def block(self, e: int, m: int) -> ApqBlock:
+        return self.host_blocks[2 * e + m]
+
+    def shared_block(self, m: int) -> ApqBlock:
+        return self.host_blocks[2 * self.E + m]
+
+
+def pack_block(idx8: np.ndarray, q: int, lut: np.ndarray):
+    """(planes, lut, rows, cols, q) for DeviceLayer from parent indices and the width-q LUT."""
+    rows, cols = idx8.shape
+    return moe_apq_pack(idx8, q), np.ascontiguousarray(lut, dtype=np.float16), rows, cols, q

@@ -1,0 +1,38 @@
+// down stage of the fused Any-Precision expert FFN, and the deterministic gate-weighted combine.
+#include "apq_engine.hpp"
+
+namespace moeapq {
+namespace apq {
+namespace {
+// y[t][r] = fp16( sum_j part[t*k + j][r] + part_shared[t][r] ), fixed summation order.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part,
+                                                      const float* __restrict__ part_shared, int T,
+                                                      int H, int k, uint16_t* __restrict__ y) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<size_t>(T) * H) return;
+  const size_t t = i / H, r = i - t * H;
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += part[(t * k + j) * H + r];
+  if (part_shared) s += part_shared[i];
+  y[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(s));
+}
+
+}  // namespace
+
+int launch_down(const KArgs& k, int max_items, hipStream_t stream) {
+  ProfileScope prof("apq_down", stream);
+  hipLaunchKernelGGL(apq_tile_kernel<kDown>, dim3(persistent_grid(max_items)), dim3(kThreads), 0,
+                     stream, k);
+  return check_launch("apq_down");
+}
+
+int launch_combine(const float* part, const float* part_shared, int T, int H, int k, uint16_t* y,
+                   hipStream_t stream) {
+  const size_t n = static_cast<size_t>(T) * H;
+  ProfileScope prof("combine", stream);
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     stream, part, part_shared, T, H, k, y);
+  return check_launch("combine");
+}
+}  // namespace apq
+}  // namespace moeapq

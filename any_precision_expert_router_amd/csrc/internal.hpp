@@ -1,0 +1,80 @@
+// Internal plumbing of libmoe_apq: error reporting, launch bookkeeping, workspace carving and
+// the launchers each kernel translation unit exports to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "moe_apq.h"
+
+namespace moeapq {
+
+// ---- error reporting (thread-local message behind moe_last_error) --------------------------
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int check_launch(const char* kernel_name);  // hipGetLastError -> MOE_EHIP + message
+
+// ---- optional kernel timer -----------------------------------------------------------------
+// Bracket a launch with events when moe_profile_start() is active on this thread.
+struct ProfileScope {
+  ProfileScope(const char* name, hipStream_t stream);
+  ~ProfileScope();
+  const char* name_;
+  hipStream_t stream_;
+  int slot_;
+};
+
+// ---- device facts ---------------------------------------------------------------------------
+int device_cu_count();  // compute units of the current device (cached per device)
+
+// ---- constants of the block format ---------------------------------------------------------
+constexpr int kRowPanel = 64;    // rows per panel: one wavefront lane per row
+constexpr int kColChunk = 128;   // columns per 16-byte unit of one plane
+constexpr int kGateUpTileRows = 32;  // gate rows (and as many up rows) per gate_up tile
+constexpr int kWavesPerTile = 4;     // wavefronts sharing one row tile (split over columns)
+
+// ---- workspace layout (all sections 256-byte aligned) ----------------------------------------
+struct Workspace {
+  int32_t* err;          // [64]: device error word + first bad (expert, module)
+  int32_t* ids;          // [T*k]   (moe_layer_forward only)
+  float* gates;          // [T*k]
+  int32_t* offsets;      // [E+1]
+  int32_t* pairs;        // [T*k]
+  int32_t* active;       // [E]
+  int32_t* n_active;     // [1]
+  uint16_t* act;         // fp16 [T*k][I]    SiLU-gated activations, sorted-pair order
+  uint16_t* act_shared;  // fp16 [T][I_shared]
+  float* part;           // fp32 [T*k][H]    gate-scaled expert outputs, pair order
+  float* part_shared;    // fp32 [T][H]      scaled shared-expert outputs
+  size_t bytes;          // total bytes the layout needs
+};
+Workspace carve_workspace(void* base, int T, int E, int H, int I, int k, int I_shared);
+
+// ---- launchers (return MOE_OK or an error code with the message set) -------------------------
+int launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
+                      hipStream_t stream);
+int launch_group_by_expert(const int32_t* ids, int T, int k, int E, int32_t* offsets,
+                           int32_t* pairs, int32_t* active, int32_t* n_active, hipStream_t stream);
+
+struct FfnArgs {
+  const moe_apq_block* table;  // device [E][2]
+  const moe_apq_block* shared; // device [2] or nullptr
+  int E, H, I, k, T, I_shared;
+  const uint16_t* x;
+  const int32_t* offsets;
+  const int32_t* pairs;
+  const int32_t* active;
+  const int32_t* n_active;
+  const float* gates;
+  const float* shared_scale;
+  uint16_t* y;
+  Workspace ws;
+};
+int launch_apq_ffn(const FfnArgs& a, hipStream_t stream);
+int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y,
+                    hipStream_t stream);
+int launch_decode_indices(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
+
+}  // namespace moeapq

@@ -1,0 +1,208 @@
+/*
+ * moe_apq.h -- C ABI of the decode-time Mixture-of-Experts layer over Any-Precision weights,
+ * native to AMD MI355X (gfx950).
+ *
+ * The layer: router logits -> softmax + top-k per token -> tokens grouped by expert -> one fused
+ * expert FFN (gate_up, SiLU(gate) * up, down, gate-weighted combine) whose weights are held as
+ * superposed bit-planes plus a per-row lookup table (LUT), with its own committed bit width per
+ * (expert, module) linear block.
+ *
+ * Sources: PagedWeight, Key Components 1 (Paged Weight Representation): weights are managed per
+ * linear block identified by (layer, expert, gate_up|down), held in the Any-Precision bit-plane +
+ * LUT format, with a desired width d_i and a committed width q_i per block in a weight page table
+ * and pages that are GPU-resident, CPU-resident or in transfer.  PagedWeight, Key Components 3: one
+ * fused kernel reads the planes and LUTs directly and mixes blocks of different widths.  LYNX,
+ * 1 Problem statement and 2.2 System Components: each token picks its own top-k experts, every
+ * token activates exactly k experts, decode cost follows the number of distinct experts a batch
+ * activates.  "Which Expert Misses Are Worth Waiting For?", Methodology: the router's first choice
+ * and normalised gate weights.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless the argument says "host".
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every device call is
+ *     asynchronous on `stream`; none reads device memory back to the host, so a sequence of calls
+ *     can be captured in a HIP graph.
+ *   - The caller owns every buffer (inputs, outputs, workspace).  Nothing is allocated or freed
+ *     inside a call, and no state is kept between calls (except the optional profiler below).
+ *   - Return value: MOE_OK (0) or a negative MOE_E* code; moe_last_error() then gives a message
+ *     (thread-local).  Arguments are validated from host-visible scalars only.  No C++ exception
+ *     crosses the ABI.
+ *   - Numbers: fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
+ */
+#ifndef MOE_APQ_H
+#define MOE_APQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* bad scalar argument (k > E, bad shape, q outside 1..8, NULL) */
+#define MOE_EUNSUPPORTED (-2) /* outside the instantiated bounds below                        */
+#define MOE_EWORKSPACE (-3)   /* workspace missing or smaller than moe_workspace_bytes()       */
+#define MOE_EHIP (-4)         /* a HIP launch or runtime call failed                           */
+#define MOE_EDEVICE (-5)      /* a kernel found an invalid block descriptor (see below)        */
+
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_TOKENS 65536
+
+/* Page states of the weight page table (PagedWeight, Key Components 1). */
+#define MOE_PAGE_GPU 0
+#define MOE_PAGE_CPU 1
+#define MOE_PAGE_IN_TRANSFER 2
+
+/*
+ * One weight-page-table entry = one (expert, module) linear block, rows x cols, read as
+ * y_r = sum_c W[r, c] x_c with W[r, c] = LUT_r[ idx_q(r, c) ].
+ *
+ *   gate_up block: rows = 2*I, cols = H; rows 0..I-1 are the gate projection, I..2I-1 the up one.
+ *   down block:    rows = H,   cols = I.
+ *   Shape rules:   rows % 64 == 0, cols % 128 == 0.
+ *
+ * planes: q bit-planes of the 8-bit parent index, plane p (0 <= p < q) holding bit 7-p, so the
+ *   q-bit index is the top-q-bit prefix of the parent index and lowering q only drops trailing
+ *   planes (no re-encoding).  Plane p is rows*cols/8 bytes at byte offset p*rows*cols/8.  Inside
+ *   a plane, the 16-byte unit of (row panel P = r/64, column chunk c4 = c/128, row-in-panel
+ *   l = r%64) sits at byte ((P*(cols/128) + c4)*64 + l)*16 and holds four little-endian words;
+ *   word j covers columns c4*128 + 32j + [0, 32), column c of a word (0..31) at bit
+ *   (8*(c/8) + 7 - p - o(c)) mod 32 with o(c) = ((c >> 1) & 3) + 4*(c & 1).  (So one wavefront
+ *   reads a row panel with 1-KiB coalesced loads and every lane owns one row.)  Write them with
+ *   moe_apq_pack().
+ * lut: fp16 [rows][2^q] row-major, entry v of row r = weight value of q-bit index v.
+ * q: committed width q_i, 1..8.  desired: d_i, carried, not read here.  state: must be
+ *   MOE_PAGE_GPU for every block a call reads (precondition; see MOE_EDEVICE).
+ * The table is an immutable snapshot for the duration of a call: width commits and page moves
+ * happen between calls, at safe boundaries (PagedWeight, Key Components 3).
+ */
+typedef struct moe_apq_block {
+  const uint32_t* planes;
+  const uint16_t* lut;
+  int32_t rows;
+  int32_t cols;
+  uint8_t q;
+  uint8_t desired;
+  uint8_t state;
+  uint8_t reserved0;
+  int32_t reserved1;
+} moe_apq_block; /* 32 bytes */
+
+/*
+ * Softmax + top-k per token (LYNX 2.2; "Which Expert Misses...", Methodology).
+ *   logits     fp32 [T][E], finite (NaN/inf: undefined result).
+ *   topk_ids   out int32 [T][k]: the k largest logits ordered by (logit desc, expert id asc);
+ *              -0.0 == +0.0, so equal values tie to the lower id.  Slot 0 is the first choice.
+ *   topk_gates out fp32 [T][k]: softmax over the k selected logits (the full softmax
+ *              renormalised over them); sums to 1 up to fp32 rounding.
+ *   Bounds: 1 <= k <= E <= MOE_MAX_EXPERTS, k <= MOE_MAX_TOPK, 0 <= T <= MOE_MAX_TOKENS (T = 0 is
+ *   a no-op).
+ */
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_gates,
+                   void* stream);
+
+/*
+ * Group the T*k (token, slot) pairs p = t*k + j by expert (LYNX 1: the set of distinct experts is
+ * what a decode batch loads).  Stable counting sort.
+ *   expert_offsets out int32 [E+1]: expert e's pairs are sorted_pairs[offsets[e] .. offsets[e+1]).
+ *   sorted_pairs   out int32 [T*k]: pair ids, expert ascending, p ascending inside an expert.
+ *   active_experts out int32 [E]: experts with >= 1 pair, ascending, then -1 padding.
+ *   n_active       out int32 [1].
+ *   workspace/ws_bytes: unused (may be NULL/0); kept for ABI stability.
+ */
+int moe_group_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t* expert_offsets,
+                        int32_t* sorted_pairs, int32_t* active_experts, int32_t* n_active,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The fused Any-Precision expert FFN over the grouped tokens (PagedWeight, Key Components 3):
+ *   for every active expert e and every pair p routed to it (token t = p / k, slot j = p % k):
+ *     h = W_gu(e) x_t;  a = SiLU(h[0:I]) * h[I:2I];  o = W_d(e) a
+ *   y_t = fp16( sum_j g_tj o_tj  +  s_t * FFN_shared(x_t) )
+ *   table        device moe_apq_block [E][2] (index e*2 + 0 = gate_up, e*2 + 1 = down).  Blocks
+ *                may each have a different q.
+ *   x            fp16 [T][H].
+ *   expert_offsets, sorted_pairs, active_experts, n_active: from moe_group_by_expert.
+ *   topk_gates   fp32 [T][k] from moe_route_topk.
+ *   shared       device moe_apq_block [2] (gate_up [2*I_shared x H], down [H x I_shared]) or
+ *                NULL (then I_shared is ignored); shared_scale fp32 [T] or NULL (= 1).
+ *   prefill_threshold: experts with at least this many routed pairs may take the dense tile path
+ *                (<= 0: library default).  Results are the same either way, up to fp32 rounding.
+ *   y            out fp16 [T][H].
+ *   workspace    >= moe_workspace_bytes(T, E, H, I, k, I_shared) bytes, 256-byte aligned.
+ *   Device checks: a routed block whose descriptor does not match (rows, cols) of its module, has
+ *   q outside 1..8 or is not MOE_PAGE_GPU is skipped and recorded in the workspace error word;
+ *   moe_check_device_error() reports it.  Accuracy: fp32 accumulation, the SiLU-gated activation
+ *   rounded once to fp16, y rounded to fp16.
+ */
+int moe_apq_ffn(const moe_apq_block* table, int E, int H, int I, const uint16_t* x, int T, int k,
+                const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                const int32_t* active_experts, const int32_t* n_active, const float* topk_gates,
+                const moe_apq_block* shared, int I_shared, const float* shared_scale,
+                int prefill_threshold, uint16_t* y, void* workspace, size_t ws_bytes,
+                void* stream);
+
+/*
+ * The whole layer: moe_route_topk + moe_group_by_expert + moe_apq_ffn, with the routing arrays
+ * kept inside the workspace.  Same arguments and rules as above.
+ */
+int moe_layer_forward(const float* logits, const uint16_t* x, int T, int E, int H, int I, int k,
+                      const moe_apq_block* table, const moe_apq_block* shared, int I_shared,
+                      const float* shared_scale, int prefill_threshold, uint16_t* y,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes moe_apq_ffn / moe_layer_forward need for these sizes (0 on bad arguments). */
+size_t moe_workspace_bytes(int T, int E, int H, int I, int k, int I_shared);
+
+/*
+ * Host-side, synchronous: pack logical 8-bit parent indices into the plane layout above.
+ *   idx8_host   host uint8 [rows][cols];  planes_host out host uint32 [q * rows * cols / 32].
+ *   Only the top q bits of each index are stored.  Packing at q and keeping the first
+ *   q' * rows*cols/32 words gives exactly the packing at q' < q.
+ */
+int moe_apq_pack(const uint8_t* idx8_host, int rows, int cols, int q, uint32_t* planes_host);
+
+/*
+ * Debug / parity: the decode GEMV engine alone on one block, no routing.
+ *   y[t][r] = sum_c W[r, c] x[t][c] for all T tokens, fp32 accumulate (the same kernel and table
+ *   lookups moe_apq_ffn uses, in its plain mode).
+ *   blk_host  host pointer to the descriptor (planes/lut are device pointers, 16-byte aligned).
+ *   x         fp16 [T][cols];  y out fp32 [T][rows].
+ */
+int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float* y, void* stream);
+
+/*
+ * Debug / parity: decode one block's q-bit indices on the GPU.
+ *   blk_host  host pointer to the descriptor (its planes pointer is a device pointer).
+ *   idx_out   device uint8 [rows][cols], row-major.
+ */
+int moe_apq_decode_indices(const moe_apq_block* blk_host, uint8_t* idx_out, void* stream);
+
+/*
+ * Synchronise `stream` and read the device error word that moe_apq_ffn / moe_layer_forward keep
+ * in `workspace`: MOE_OK if clean, MOE_EDEVICE (with a message naming the first bad block)
+ * otherwise.  Clears the word.
+ */
+int moe_check_device_error(void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Optional kernel timer (tracing).  moe_profile_start() makes every later device call on this
+ * thread bracket each kernel it launches with HIP events on the call's stream.
+ * moe_profile_stop() synchronises those streams, stops recording and returns the number of
+ * distinct kernels; for each (up to max_kernels) it writes the name (NUL-terminated, at most 63
+ * chars, into names_out + 64*i), the summed milliseconds and the launch count.
+ */
+int moe_profile_start(void);
+int moe_profile_stop(int max_kernels, char* names_out, double* total_ms_out,
+                     int32_t* launches_out);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_APQ_H */

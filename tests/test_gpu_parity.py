@@ -1,0 +1,270 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: top-k ids, the grouping (offsets, pairs, active list), decoded indices and one-hot
+GEMV probes.  Floating point: gates within 1e-6 absolute (fp32 softmax of the same fp32 logits),
+the single-block GEMV within 1e-5 relative L2 (fp32 accumulation of exact fp16 products), and
+layer outputs within 1e-3 relative L2 (fp32 accumulation, the SiLU-gated activation rounded
+once to fp16, y rounded to fp16: about 4e-4 expected).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+import any_precision_expert_router_amd as apq  # noqa: E402  (fails loudly if not built)
+import gpu_layers  # noqa: E402
+
+DEV = "cuda"
+LAYER_TOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _t(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(DEV) if dtype is None else t.to(DEV, dtype)
+
+
+def _route_gpu(logits, k):
+    T, E = logits.shape
+    lt = _t(logits.astype(np.float32))
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    gates = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    apq.moe_route_topk(lt, k, ids, gates)
+    return ids, gates
+
+
+def _group_gpu(ids, E):
+    T, k = ids.shape
+    off = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    pairs = torch.empty(max(T * k, 1), dtype=torch.int32, device=DEV)
+    act = torch.empty(E, dtype=torch.int32, device=DEV)
+    nact = torch.empty(1, dtype=torch.int32, device=DEV)
+    apq.moe_group_by_expert(ids, E, off, pairs, act, nact)
+    return off, pairs[: T * k], act, nact
+
+
+# ------------------------------------------------------------------------------------------
+# routing and grouping: bit-exact
+# ------------------------------------------------------------------------------------------
+ROUTE_CASES = [(4, 8, 2), (16, 60, 4), (64, 512, 10), (33, 64, 8), (7, 1024, 32), (5, 3, 3),
+               (2048, 64, 8), (1, 1, 1), (9, 128, 1)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES)
+def test_route_topk_bit_exact(T, E, k):
+    say(f"route T={T} E={E} k={k}")
+    r = np.random.default_rng(T * 7 + E + k)
+    logits = (r.standard_normal((T, E)) * 2).astype(np.float16).astype(np.float32)  # ties
+    if T > 2:
+        logits[0] = 0.25
+        logits[1, ::2] = -0.0
+        logits[1, 1::2] = 0.0
+    ids, gates = _route_gpu(logits, k)
+    ref_ids, ref_g = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    g = gates.cpu().numpy()
+    np.testing.assert_allclose(g, ref_g, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(g.sum(1), 1.0, atol=1e-6)
+
+
+def test_route_zipf_router_bit_exact():
+    shape = wl.QWEN3_NEXT_80B_A3B
+    inp = wl.gen_layer_inputs(shape)
+    ids, gates = _route_gpu(inp.logits, shape.k)
+    ref_ids, ref_g = oracle.route_topk(inp.logits, shape.k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(gates.cpu().numpy(), ref_g, atol=1e-6)
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES + [(0, 8, 2), (40, 16, 16)])
+def test_group_by_expert_bit_exact(T, E, k):
+    say(f"group T={T} E={E} k={k}")
+    r = np.random.default_rng(T + 3 * E + k)
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    if T:
+        logits[:, 0] += 4.0   # a hot expert
+    ref_ids, _ = oracle.route_topk(logits, k)
+    ids = _t(ref_ids.astype(np.int32))
+    off, pairs, act, nact = _group_gpu(ids, E)
+    r_off, r_pairs, r_act, r_n = oracle.group_by_expert(ref_ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), r_off)
+    np.testing.assert_array_equal(pairs.cpu().numpy(), r_pairs)
+    np.testing.assert_array_equal(act.cpu().numpy(), r_act)
+    assert int(nact.item()) == r_n
+
+
+def test_group_single_expert_takes_every_token():
+    T, E, k = 300, 64, 1
+    ids = np.full((T, k), 5, dtype=np.int32)
+    off, pairs, act, nact = _group_gpu(_t(ids), E)
+    r_off, r_pairs, r_act, r_n = oracle.group_by_expert(ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), r_off)
+    np.testing.assert_array_equal(pairs.cpu().numpy(), r_pairs)
+    assert int(nact.item()) == 1 and int(act[0].item()) == 5
+
+
+# ------------------------------------------------------------------------------------------
+# bit-plane decoding and the decode GEMV engine
+# ------------------------------------------------------------------------------------------
+def _upload_block(idx8, q, lut):
+    planes = apq.moe_apq_pack(idx8, q)
+    pt = _t(planes.view(np.int32))
+    lt = _t(np.ascontiguousarray(lut, dtype=np.float16).view(np.int16))
+    blk = apq.ApqBlock(pt.data_ptr(), lt.data_ptr(), idx8.shape[0], idx8.shape[1], q, q, 0, 0, 0)
+    return blk, (pt, lt)
+
+
+@pytest.mark.parametrize("q", range(1, 9))
+def test_decode_indices_bit_exact(q):
+    r = np.random.default_rng(q)
+    idx8 = r.integers(0, 256, size=(192, 384), dtype=np.uint8)
+    lut = r.standard_normal((192, 1 << q)).astype(np.float16)
+    blk, keep = _upload_block(idx8, q, lut)
+    out = torch.empty((192, 384), dtype=torch.uint8, device=DEV)
+    apq.moe_apq_decode_indices(blk, out)
+    np.testing.assert_array_equal(out.cpu().numpy(), oracle.committed_index(idx8, q))
+
+
+@pytest.mark.parametrize("q", range(1, 9))
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 16, 17, 40])
+def test_gemv_matches_oracle(q, T):
+    say(f"gemv q={q} T={T}")
+    R, C = 128, 640
+    r = np.random.default_rng(q * 100 + T)
+    idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
+    lut = (np.sort(r.standard_normal((R, 1 << q)), axis=1) * 0.02).astype(np.float16)
+    x = r.standard_normal((T, C)).astype(np.float16)
+    blk, keep = _upload_block(idx8, q, lut)
+    y = torch.empty((T, R), dtype=torch.float32, device=DEV)
+    apq.moe_apq_gemv(blk, _t(x), y)
+    ref = oracle.apq_matvec(oracle.committed_index(idx8, q), lut, x.astype(np.float64).T).T
+    assert oracle.rel_l2(y.cpu().numpy(), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("q", range(1, 9))
+def test_gemv_one_hot_probe_is_exact_lut_read(q):
+    """x = e_c gives y_r = LUT_r[idx_q(r, c)] exactly: pins the decode through the GEMV."""
+    R, C = 64, 256
+    r = np.random.default_rng(50 + q)
+    idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
+    lut = r.standard_normal((R, 1 << q)).astype(np.float16)
+    cols = [0, 1, 31, 32, 77, 128, 200, 255]
+    x = np.zeros((len(cols), C), dtype=np.float16)
+    for t, c in enumerate(cols):
+        x[t, c] = 1.0
+    blk, keep = _upload_block(idx8, q, lut)
+    y = torch.empty((len(cols), R), dtype=torch.float32, device=DEV)
+    apq.moe_apq_gemv(blk, _t(x), y)
+    idx = oracle.committed_index(idx8, q)
+    expect = np.stack([lut[np.arange(R), idx[:, c]].astype(np.float32) for c in cols])
+    np.testing.assert_array_equal(y.cpu().numpy(), expect)
+
+
+# ------------------------------------------------------------------------------------------
+# the layer
+# ------------------------------------------------------------------------------------------
+def _run_layer(shape, inputs, dl, shared_scale=None):
+    T = shape.T
+    y = torch.empty((T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(T, shape.E, shape.H, shape.I, shape.k, shape.I_shared),
+                     dtype=torch.uint8, device=DEV)
+    ss = None if shared_scale is None else _t(shared_scale.astype(np.float32))
+    apq.moe_layer_forward(_t(inputs.logits), _t(inputs.x), shape.E, shape.H, shape.I, shape.k, dl.table,
+                          y, ws, shared=dl.shared, I_shared=shape.I_shared, shared_scale=ss)
+    apq.moe_check_device_error(ws)
+    return y.float().cpu().numpy().astype(np.float64), ws
+
+
+def _check_layer(shape, q_override=None, shared_scale=None, tokens=None, seed=0):
+    inputs = wl.gen_layer_inputs(shape, seed)
+    dl = gpu_layers.device_layer(shape, q_override=q_override)
+    y, _ = _run_layer(shape, inputs, dl, shared_scale)
+    get, sh = gpu_layers.oracle_getters(shape, q_override)
+    ref = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh,
+                               shared_scale=shared_scale, tokens=tokens)
+    rows = slice(None) if tokens is None else list(tokens)
+    err = oracle.rel_l2(y[rows], ref["y"][rows])
+    say(f"  {shape.name} T={shape.T}: rel L2 = {err:.3e}")
+    assert err <= LAYER_TOL
+    return y, ref
+
+
+def test_layer_tiny():
+    _check_layer(wl.TINY)
+
+
+def test_layer_every_width_in_one_call_ragged_tokens():
+    shape = wl.TINY.replace(H=256, E=12, I=384, k=3, T=21, name="mixed widths 1..8")
+    q = np.array([[1 + (2 * e + m) % 8 for m in range(2)] for e in range(shape.E)], dtype=np.uint8)
+    _check_layer(shape, q_override=q)
+
+
+def test_layer_with_shared_expert_and_scale():
+    shape = wl.TINY.replace(H=256, E=8, I=256, k=2, T=19, I_shared=512, q_shared=8, name="shared")
+    r = np.random.default_rng(3)
+    _check_layer(shape, shared_scale=r.uniform(-1, 2, size=shape.T))
+
+
+def test_layer_k1_and_k_equals_E():
+    _check_layer(wl.TINY.replace(k=1, T=9, name="k=1"))
+    _check_layer(wl.TINY.replace(k=8, T=6, name="k=E"))
+
+
+def test_layer_many_tokens_on_one_expert():
+    """More than one 16-token group per expert (tokens beyond the group re-use the tile)."""
+    shape = wl.TINY.replace(E=4, k=2, T=70, name="hot experts")
+    _check_layer(shape)
+
+
+def test_layer_is_deterministic():
+    shape = wl.TINY.replace(T=13, name="determinism")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    y1, _ = _run_layer(shape, inputs, dl)
+    y2, _ = _run_layer(shape, inputs, dl)
+    np.testing.assert_array_equal(y1, y2)
+
+
+def test_layer_components_match_layer_forward():
+    """route -> group -> ffn through the separate entry points equals moe_layer_forward."""
+    shape = wl.TINY.replace(T=11, name="components")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    y_full, _ = _run_layer(shape, inputs, dl)
+    ids, gates = _route_gpu(inputs.logits, shape.k)
+    off, pairs, act, nact = _group_gpu(ids, shape.E)
+    y = torch.empty((shape.T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(shape.T, shape.E, shape.H, shape.I, shape.k, 0),
+                     dtype=torch.uint8, device=DEV)
+    apq.moe_apq_ffn(dl.table, shape.E, shape.H, shape.I, _t(inputs.x), shape.k, off, pairs, act, nact,
+                    gates, y, ws)
+    np.testing.assert_array_equal(y.float().cpu().numpy(), y_full)
+
+
+def test_invalid_descriptor_is_reported_not_read():
+    shape = wl.TINY.replace(T=4, name="bad descriptor")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    table = dl.table.clone().view(torch.uint8).reshape(shape.E * 2, 32)
+    table[:, 24] = 9          # q = 9 on every block
+    y = torch.empty((shape.T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(shape.T, shape.E, shape.H, shape.I, shape.k, 0),
+                     dtype=torch.uint8, device=DEV)
+    apq.moe_layer_forward(_t(inputs.logits), _t(inputs.x), shape.E, shape.H, shape.I, shape.k,
+                          table.reshape(-1), y, ws)
+    with pytest.raises(apq.MoeError) as ei:
+        apq.moe_check_device_error(ws)
+    assert ei.value.code == apq.MOE_EDEVICE
+    apq.moe_check_device_error(ws)    # cleared by the read
