@@ -71,7 +71,7 @@ def _load():
         "moe_layer_forward": ([P, P, I, I, I, I, I, P, P, I, P, I, P, P, Z, S], I),
         "moe_workspace_bytes": ([I, I, I, I, I, I], Z),
         "moe_apq_pack": ([P, I, I, I, P], I),
-        "moe_apq_gemv": ([P, P, I, P, S], I),
+        "moe_apq_gemv": ([P, P, I, P, I, S], I),
         "moe_apq_decode_indices": ([P, P, S], I),
         "moe_check_device_error": ([P, Z, S], I),
         "moe_profile_start": ([], I),
@@ -167,10 +167,10 @@ def moe_apq_pack(idx8: np.ndarray, q: int) -> np.ndarray:
     return out
 
 
-def moe_apq_gemv(block: ApqBlock, x, y, stream=None) -> None:
+def moe_apq_gemv(block: ApqBlock, x, y, dense_threshold: int = 0, stream=None) -> None:
     """Decode GEMV on one block: x fp16 [T, cols] -> y fp32 [T, rows]."""
     _check("moe_apq_gemv", _lib.moe_apq_gemv(ctypes.byref(block), _ptr(x), x.shape[0], _ptr(y),
-                                             _stream(stream)))
+                                             dense_threshold, _stream(stream)))
 
 
 def moe_apq_decode_indices(block: ApqBlock, idx_out, stream=None) -> None:

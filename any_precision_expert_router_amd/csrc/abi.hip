@@ -197,7 +197,6 @@ int moe_apq_ffn(const moe_apq_block* table, int E, int H, int I, const uint16_t*
                 const moe_apq_block* shared, int I_shared, const float* shared_scale,
                 int prefill_threshold, uint16_t* y, void* workspace, size_t ws_bytes,
                 void* stream) {
-  (void)prefill_threshold;
   clear_error();
   if (int rc = check_route_args(T, E, k)) return rc;
   if (int rc = check_ffn_dims(H, I, I_shared, shared != nullptr)) return rc;
@@ -211,7 +210,7 @@ int moe_apq_ffn(const moe_apq_block* table, int E, int H, int I, const uint16_t*
     return set_error(MOE_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                      ws.bytes);
   FfnArgs a{table, shared, E, H, I, k, T, ish, x, expert_offsets, sorted_pairs, active_experts,
-            n_active, topk_gates, shared_scale, y, ws};
+            n_active, topk_gates, shared_scale, y, ws, prefill_threshold};
   return launch_apq_ffn(a, as_stream(stream));
 }
 
@@ -219,7 +218,6 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int T, int E, int 
                       const moe_apq_block* table, const moe_apq_block* shared, int I_shared,
                       const float* shared_scale, int prefill_threshold, uint16_t* y,
                       void* workspace, size_t ws_bytes, void* stream) {
-  (void)prefill_threshold;
   clear_error();
   if (int rc = check_route_args(T, E, k)) return rc;
   if (int rc = check_ffn_dims(H, I, I_shared, shared != nullptr)) return rc;
@@ -235,11 +233,12 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int T, int E, int 
   if (int rc = launch_group_by_expert(ws.ids, T, k, E, ws.offsets, ws.pairs, ws.active, ws.n_active, s))
     return rc;
   FfnArgs a{table, shared, E, H, I, k, T, ish, x, ws.offsets, ws.pairs, ws.active, ws.n_active,
-            ws.gates, shared_scale, y, ws};
+            ws.gates, shared_scale, y, ws, prefill_threshold};
   return launch_apq_ffn(a, s);
 }
 
-int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float* y, void* stream) {
+int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float* y,
+                 int dense_threshold, void* stream) {
   clear_error();
   if (int rc = check_block_host(blk_host)) return rc;
   if (T < 0 || T > MOE_MAX_TOKENS) return set_error(MOE_EUNSUPPORTED, "T=%d outside 0..%d", T, MOE_MAX_TOKENS);
@@ -247,7 +246,7 @@ int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float*
   if (!x || !y) return set_error(MOE_EINVAL, "NULL pointer argument");
   moe_apq_block b = *blk_host;
   b.state = MOE_PAGE_GPU;
-  return launch_apq_gemv(b, x, T, y, as_stream(stream));
+  return launch_apq_gemv(b, x, T, y, dense_threshold, as_stream(stream));
 }
 
 int moe_apq_decode_indices(const moe_apq_block* blk_host, uint8_t* idx_out, void* stream) {

@@ -31,6 +31,8 @@ namespace apq {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Address-space qualified views: plane and LUT reads are per-lane global loads; activation rows
 // and the routing arrays, read at wavefront-uniform addresses and never written during the
@@ -45,11 +47,11 @@ template <class T>
 MOE_INLINE const AS_CONST T* cview(const void* p) { return (const AS_CONST T*)p; }
 
 constexpr int kThreads = 64 * kWavesPerTile;
-constexpr int kMaxTokGroup = 16;                 // tokens sharing one pass over the weights
+constexpr int kMaxTokGroup = 4;                  // tokens sharing one VALU pass over the weights
 constexpr int kTblWords = 256 * 64;              // [256 entries][64 lanes] uint32
-constexpr int kRawWords = 16 * 64 / 2;           // PAIR staging: [16 entries][64 lanes] fp16
-constexpr int kRedWords = (kWavesPerTile - 1) * kMaxTokGroup * 64;
-constexpr int kLdsWords = kTblWords + kRawWords + kRedWords;
+constexpr int kDenseGroup = 16;                  // tokens per MFMA pass (32x32 tile: 2 row halves x 16)
+constexpr int kRedWords = (kWavesPerTile - 1) * 16 * 64;  // 16 floats per lane per wavefront
+constexpr int kLdsWords = kTblWords + kRedWords;
 
 // The only LDS object of the tile kernels, so the table starts at LDS address 0 and a table
 // address is exactly entry*256 + lane*4.
@@ -113,70 +115,21 @@ MOE_INLINE uint32_t word_of(const u32x4& v, int jw) {
   return jw == 0 ? v.x : jw == 1 ? v.y : jw == 2 ? v.z : v.w;
 }
 
-// One wavefront's share of the columns of a row tile: acc[t] += sum_c W[row(lane), c] x_t[c].
-//   pbase: this lane's 16-byte unit of plane 0 in chunk 0; plane_u4: 16-byte units per plane.
-//   xr[t]: token t's activation row as dwords (two fp16), wavefront-uniform.
-template <int Q, int NT>
-MOE_INLINE void tile_columns(const AS_GLOBAL u32x4* pbase, size_t plane_u4, int c_begin, int c_end,
-                             const AS_CONST uint32_t* const (&xr)[NT], uint32_t lane4,
-                             float (&acc)[NT]) {
-  if (c_begin >= c_end) return;
-  u32x4 cur[Q], nxt[Q];
-#pragma unroll
-  for (int p = 0; p < Q; ++p) cur[p] = pbase[p * plane_u4 + static_cast<size_t>(c_begin) * 64];
-  for (int c4 = c_begin; c4 < c_end; ++c4) {
-    const bool more = c4 + 1 < c_end;
-    if (more) {
-#pragma unroll
-      for (int p = 0; p < Q; ++p) nxt[p] = pbase[p * plane_u4 + static_cast<size_t>(c4 + 1) * 64];
-    }
-#pragma unroll
-    for (int jw = 0; jw < 4; ++jw) {
-      uint32_t w[Q];
-#pragma unroll
-      for (int p = 0; p < Q; ++p) w[p] = word_of(cur[p], jw);
-      const int xoff = c4 * 64 + jw * 16;  // dword offset of this word's 32 columns
-      uint32_t wv[16];                     // packed (even, odd) weights, dword d = 4b + j
-      if constexpr (Q <= 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t pw = pair_word<Q>(w, j);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) wv[4 * b + j] = lds_load(tbl_addr(pw, lane4, b));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t we = single_word<Q>(w, j), wo = single_word<Q>(w, j + 4);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t ve = lds_load(tbl_addr(we, lane4, b));
-            const uint32_t vo = lds_load(tbl_addr(wo, lane4, b));
-            wv[4 * b + j] = __builtin_amdgcn_perm(vo, ve, 0x05040100u);  // (even lo, odd hi)
-          }
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int d = 0; d < 16; ++d) acc[t] = dot2(wv[d], xr[t][xoff + d], acc[t]);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int p = 0; p < Q; ++p) cur[p] = nxt[p];
-    }
-  }
-}
+constexpr int kLutRegs = 8;  // 16-byte LUT registers one thread prefetches for an item
+
+// Depth of the per-wavefront ring of in-flight 128-column chunks (all q planes of a chunk).
+template <int Q>
+constexpr int ring_depth() { return Q <= 4 ? 4 : (Q == 5 ? 3 : 2); }
 
 struct Item {
   const uint32_t* planes;
   const uint16_t* lut;
-  int rows, cols;
-  int r0;        // first row of the tile (first gate row for gate_up)
+  int rows, cols, q;
+  int r0;        // row of lane 0 (first gate row for gate_up)
   int row_hi;    // row of lane 32 (gate_up: first up row)
   int n;         // tokens routed to the tile
   int src_base;  // sorted position of the expert's first pair (routed), 0 (shared/plain)
+  int expert;    // routed expert id, -1 for the shared expert / plain block
   bool shared;
 };
 
@@ -198,86 +151,222 @@ struct KArgs {
   float* part_shared;           // fp32 [T][H]
   float* y_plain;               // fp32 [T][rows]
   int32_t* err;
+  int dense_threshold;          // tiles with at least this many tokens take the MFMA path
 };
 
-// Build the row tile's lookup table in LDS: [entry][lane] 4-byte slots.
-//   PAIR  (q <= 4): entry (a << 4 | b) = LUT_row[a] | LUT_row[b] << 16.
-//   SINGLE (q >= 5): entry v = LUT_row[v] in both halves.
-template <int Q>
-MOE_INLINE void build_table(const uint16_t* lut, int row_lo, int row_hi) {
-  const int tid = threadIdx.x;
-  constexpr int NE = 1 << Q;
-  constexpr int kPer = NE >= 8 ? 8 : NE;   // LUT entries one thread moves per step
-  constexpr int kChunks = NE / kPer;
-  uint16_t* raw = reinterpret_cast<uint16_t*>(g_lds + kTblWords);
-  const AS_GLOBAL uint16_t* L = gview<uint16_t>(lut);
-  for (int i = tid; i < 64 * kChunks; i += kThreads) {
-    const int l = i & 63, ch = i >> 6;
-    const int row = l < 32 ? row_lo + l : row_hi + (l - 32);
-    const AS_GLOBAL uint16_t* src = L + static_cast<size_t>(row) * NE + ch * kPer;
-    uint16_t v[8];
-    if constexpr (NE >= 8) {
-      const u32x4 u = *reinterpret_cast<const AS_GLOBAL u32x4*>(src);
-      v[0] = u.x & 0xffff; v[1] = u.x >> 16; v[2] = u.y & 0xffff; v[3] = u.y >> 16;
-      v[4] = u.z & 0xffff; v[5] = u.z >> 16; v[6] = u.w & 0xffff; v[7] = u.w >> 16;
-    } else {
-#pragma unroll
-      for (int m = 0; m < kPer; ++m) v[m] = src[m];
+MOE_INLINE int lane_row(const Item& it, int lane) {
+  return lane < 32 ? it.r0 + lane : it.row_hi + (lane - 32);
+}
+
+// Each thread prefetches LUT bytes of its lane's row into registers:
+//   q <= 4: the whole row (2^q fp16, at most 32 bytes), every wavefront (they build different
+//           first indices of the pair table);
+//   q >= 5: quarter `wave` of the row (2^(q-2) fp16, at most 128 bytes).
+MOE_INLINE void prefetch_lut(const Item& it, int lane, int wave, u32x4 (&L)[kLutRegs]) {
+  const char* row = reinterpret_cast<const char*>(it.lut) +
+                    static_cast<size_t>(lane_row(it, lane)) * (2u << it.q);
+  const AS_GLOBAL char* g = gview<char>(row);
+  switch (it.q) {
+    case 1: L[0].x = *reinterpret_cast<const AS_GLOBAL uint32_t*>(g); break;
+    case 2: {
+      const uint64_t v = *reinterpret_cast<const AS_GLOBAL uint64_t*>(g);
+      L[0].x = static_cast<uint32_t>(v);
+      L[0].y = static_cast<uint32_t>(v >> 32);
+      break;
     }
+    case 3: L[0] = *reinterpret_cast<const AS_GLOBAL u32x4*>(g); break;
+    case 4:
+      L[0] = reinterpret_cast<const AS_GLOBAL u32x4*>(g)[0];
+      L[1] = reinterpret_cast<const AS_GLOBAL u32x4*>(g)[1];
+      break;
+    default: {
+      const int n4 = 1 << (it.q - 5);  // 1, 2, 4, 8 registers
+      const AS_GLOBAL u32x4* s = reinterpret_cast<const AS_GLOBAL u32x4*>(g) + wave * n4;
 #pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int e = ch * kPer + m;
-      if constexpr (Q <= 4) raw[e * 64 + l] = v[m];
-      else g_lds[e * 64 + l] = static_cast<uint32_t>(v[m]) * 0x00010001u;
-    }
-  }
-  if constexpr (Q <= 4) {
-    __syncthreads();
-    for (int i = tid; i < NE * NE * 64; i += kThreads) {
-      const int l = i & 63, e = i >> 6;
-      const int a = e >> Q, b = e & (NE - 1);
-      g_lds[((a << 4) | b) * 64 + l] =
-          static_cast<uint32_t>(raw[a * 64 + l]) | (static_cast<uint32_t>(raw[b * 64 + l]) << 16);
+      for (int r = 0; r < kLutRegs; ++r)
+        if (r < n4) L[r] = s[r];
+      break;
     }
   }
 }
 
-template <int MODE, int Q, int NT>
-MOE_INLINE void run_group(const KArgs& A, const Item& it, int g0, int ng) {
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);  // uniform per wavefront
-  const int C = it.cols;
-  // --- the activation rows of the group's tokens (uniform); padding slots repeat slot 0 ---
-  const AS_CONST uint32_t* xr[NT];
+// fp16 number h (0-based) of the prefetched registers, as the byte pair a v_perm selects.
+MOE_INLINE uint32_t lut_dword(const u32x4 (&L)[kLutRegs], int h) { return word_of(L[h >> 3], (h >> 1) & 3); }
+
+// Write this thread's part of the row tile's table from the prefetched registers.
+//   PAIR  (q <= 4): entry (a << 4 | b) = LUT[a] | LUT[b] << 16; wave w writes the a in its quarter.
+//   SINGLE (q >= 5): entry v = LUT[v] in both halves; wave w writes its quarter of v.
+// Addresses are lane*4 + constant, so every write is one ds_write_b32 with an immediate offset.
+template <int Q, int W>
+MOE_INLINE void write_pair_rows(const u32x4 (&L)[kLutRegs], char* base) {
+  constexpr int NE = 1 << Q;
+  constexpr int APW = NE >= 4 ? NE / 4 : 1;  // first indices per wavefront
+  if constexpr (W * APW < NE) {
+#pragma unroll
+    for (int ai = 0; ai < APW; ++ai) {
+      const int a = W * APW + ai;
+      const uint32_t da = lut_dword(L, a);
+#pragma unroll
+      for (int b = 0; b < NE; ++b) {
+        const uint32_t db = lut_dword(L, b);
+        const uint32_t sel = ((a & 1) ? 0x0302u : 0x0100u) | ((b & 1) ? 0x07060000u : 0x05040000u);
+        *reinterpret_cast<uint32_t*>(base + (((a << 4) | b) << 8)) = __builtin_amdgcn_perm(db, da, sel);
+      }
+    }
+  }
+}
+
+template <int Q>
+MOE_INLINE void write_table(const u32x4 (&L)[kLutRegs], int lane, int wave) {
+  constexpr int NE = 1 << Q;
+  char* base = reinterpret_cast<char*>(g_lds) + lane * 4;
+  if constexpr (Q <= 4) {
+    switch (wave) {
+      case 0: write_pair_rows<Q, 0>(L, base); break;
+      case 1: write_pair_rows<Q, 1>(L, base); break;
+      case 2: write_pair_rows<Q, 2>(L, base); break;
+      default: write_pair_rows<Q, 3>(L, base); break;
+    }
+  } else {
+    constexpr int VPW = NE / 4;  // entries per wavefront
+    char* wbase = base + wave * (VPW << 8);
+#pragma unroll
+    for (int vi = 0; vi < VPW; ++vi) {
+      const uint32_t d = lut_dword(L, vi);
+      const uint32_t dup = __builtin_amdgcn_perm(d, d, (vi & 1) ? 0x03020302u : 0x01000100u);
+      *reinterpret_cast<uint32_t*>(wbase + (vi << 8)) = dup;
+    }
+  }
+}
+
+// One 32-column word: the row's 32 weights as 16 packed (even, odd) fp16 pairs, dword d = 4b + j
+// covering columns 8b + 2j and 8b + 2j + 1.
+template <int Q>
+MOE_INLINE void decode_word(const uint32_t (&w)[Q], uint32_t lane4, uint32_t (&wv)[16]) {
+  if constexpr (Q <= 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t pw = pair_word<Q>(w, j);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) wv[4 * b + j] = lds_load(tbl_addr(pw, lane4, b));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t we = single_word<Q>(w, j), wo = single_word<Q>(w, j + 4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t ve = lds_load(tbl_addr(we, lane4, b));
+        const uint32_t vo = lds_load(tbl_addr(wo, lane4, b));
+        wv[4 * b + j] = __builtin_amdgcn_perm(vo, ve, 0x05040100u);  // (even lo, odd hi)
+      }
+    }
+  }
+}
+
+// acc += dot(w, x) with x broadcast from lane N of each 16-lane row (DPP row_newbcast): every
+// lane of a row holds 4 dwords of the activations, so one 16-byte load per lane per chunk gives
+// the whole row the chunk's 64 dwords.  The x registers come straight from vector loads (no VALU
+// write precedes the DPP read, so no extra wait states are needed).
+template <int N>
+MOE_INLINE float dot2_bcast(float acc, uint32_t w, uint32_t x) {
+  asm("v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc)
+      : "v"(x), "v"(w), "i"(N));
+  return acc;
+}
+
+// The wavefront's chunk stream: its column chunks [cb, ce) of the tile, with the q plane units
+// and the NT tokens' activation dwords of each chunk loaded D chunks ahead.  Planes and
+// activations share the in-order vector-memory counter, so waiting for one chunk never waits on
+// anything issued later.
+template <int Q, int NT>
+struct Stream {
+  static constexpr int D = ring_depth<Q>();
+  u32x4 buf[D][Q];
+  u32x4 xbuf[D][NT];
+  const AS_GLOBAL u32x4* pbase;       // this lane's unit of plane 0, chunk 0
+  const AS_GLOBAL u32x4* xbase[NT];   // token t's row + this lane's 16 bytes of chunk 0
+  size_t plane_u4;
+  int cb, ce;
+
+  MOE_INLINE void issue(int slot, int c) {
+#pragma unroll
+    for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u4 + static_cast<size_t>(c) * 64];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xbuf[slot][t] = xbase[t][static_cast<size_t>(c) * 16];
+  }
+  MOE_INLINE void prologue() {
+#pragma unroll
+    for (int s = 0; s < D; ++s)
+      if (cb + s < ce) issue(s, cb + s);
+  }
+};
+
+template <int Q, int NT, int JW>
+MOE_INLINE void word_products(const Stream<Q, NT>& S, int s, const uint32_t (&wv)[16], float (&acc)[NT]) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int tt = g0 + (t < ng ? t : 0);
-    const uint16_t* row;
-    if constexpr (MODE == kGateUp) {
-      const int tok = it.shared ? tt : uniform(cview<int32_t>(A.pairs)[it.src_base + tt]) / A.k;
-      row = A.x + static_cast<size_t>(tok) * C;
-    } else if constexpr (MODE == kDown) {
-      row = it.shared ? A.act_shared + static_cast<size_t>(tt) * C
-                      : A.act + static_cast<size_t>(it.src_base + tt) * C;
-    } else {
-      row = A.x + static_cast<size_t>(tt) * C;
-    }
-    xr[t] = cview<uint32_t>(row);
+    const u32x4& xv = S.xbuf[s][t];
+    // dword d of word JW is dword 16*JW + d of the chunk: lane 4*JW + d/4, component d%4
+    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[0], xv.x);
+    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[1], xv.y);
+    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[2], xv.z);
+    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[3], xv.w);
+    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[4], xv.x);
+    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[5], xv.y);
+    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[6], xv.z);
+    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[7], xv.w);
+    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[8], xv.x);
+    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[9], xv.y);
+    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[10], xv.z);
+    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[11], xv.w);
+    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[12], xv.x);
+    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[13], xv.y);
+    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[14], xv.z);
+    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[15], xv.w);
   }
-  // --- this lane's row and its first plane unit ---
-  const int row = lane < 32 ? it.r0 + lane : it.row_hi + (lane - 32);
-  const int nc4 = C / kColChunk;
-  const AS_GLOBAL u32x4* pbase = gview<u32x4>(it.planes) +
-                                 static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
-  const size_t plane_u4 = static_cast<size_t>(it.rows) * C / 128;
-  const int c_begin = (nc4 * wave) / kWavesPerTile, c_end = (nc4 * (wave + 1)) / kWavesPerTile;
-  float acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-  tile_columns<Q, NT>(pbase, plane_u4, c_begin, c_end, xr, static_cast<uint32_t>(lane) * 4u, acc);
+}
 
-  // --- cross-wavefront reduction in a fixed order: wave 0 + 1 + 2 + 3 ---
-  float* red = reinterpret_cast<float*>(g_lds + kTblWords + kRawWords);
+template <int Q, int NT, int JW>
+MOE_INLINE void one_word(const Stream<Q, NT>& S, int s, uint32_t lane4, float (&acc)[NT]) {
+  uint32_t w[Q];
+#pragma unroll
+  for (int p = 0; p < Q; ++p) w[p] = word_of(S.buf[s][p], JW);
+  uint32_t wv[16];
+  decode_word<Q>(w, lane4, wv);
+  word_products<Q, NT, JW>(S, s, wv, acc);
+  // keep the next word's lookups below this word's products: bounds live registers
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// acc[t] += sum over the stream's columns of W[row(lane), c] x_t[c]; consumes the ring that
+// prologue() filled and refills each slot D chunks ahead once its chunk is decoded.
+template <int Q, int NT>
+MOE_INLINE void stream_columns(Stream<Q, NT>& S, uint32_t lane4, float (&acc)[NT]) {
+  constexpr int D = Stream<Q, NT>::D;
+  for (int c0 = S.cb; c0 < S.ce; c0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int c = c0 + s;
+      if (c < S.ce) {
+        one_word<Q, NT, 0>(S, s, lane4, acc);
+        one_word<Q, NT, 1>(S, s, lane4, acc);
+        one_word<Q, NT, 2>(S, s, lane4, acc);
+        one_word<Q, NT, 3>(S, s, lane4, acc);
+        if (c + D < S.ce) S.issue(s, c + D);
+      }
+    }
+  }
+}
+
+// Reduce the four wavefronts' partial sums (fixed order: wave 0 + 1 + 2 + 3) and apply the
+// epilogue of the mode for the ng real tokens of the group starting at g0.
+template <int MODE, int NT>
+MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, float (&acc)[NT]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  float* red = reinterpret_cast<float*>(g_lds + kTblWords);
   if (wave > 0) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[((wave - 1) * kMaxTokGroup + t) * 64 + lane] = acc[t];
@@ -319,18 +408,50 @@ MOE_INLINE void run_group(const KArgs& A, const Item& it, int g0, int ng) {
   __syncthreads();
 }
 
-template <int MODE, int Q>
-MOE_INLINE void run_item(const KArgs& A, const Item& it) {
-  build_table<Q>(it.lut, it.r0, it.row_hi);
-  __syncthreads();
-  for (int g0 = 0; g0 < it.n; g0 += kMaxTokGroup) {
-    const int ng = min(kMaxTokGroup, it.n - g0);
-    if (ng == 1) run_group<MODE, Q, 1>(A, it, g0, ng);
-    else if (ng == 2) run_group<MODE, Q, 2>(A, it, g0, ng);
-    else if (ng <= 4) run_group<MODE, Q, 4>(A, it, g0, ng);
-    else if (ng <= 8) run_group<MODE, Q, 8>(A, it, g0, ng);
-    else run_group<MODE, Q, 16>(A, it, g0, ng);
+// The chunk stream of token group [g0, g0 + ng) for this wavefront (prologue not yet issued).
+template <int MODE, int Q, int NT>
+MOE_INLINE void make_stream(const KArgs& A, const Item& it, int g0, int ng, Stream<Q, NT>& S) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int C = it.cols;
+  const int row = lane_row(it, lane);
+  const int nc4 = C / kColChunk;
+  S.pbase = gview<u32x4>(it.planes) + static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
+  S.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
+  S.cb = uniform((nc4 * wave) / kWavesPerTile);
+  S.ce = uniform((nc4 * (wave + 1)) / kWavesPerTile);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tt = g0 + (t < ng ? t : 0);  // padding slots repeat slot 0
+    const uint16_t* rowp;
+    if constexpr (MODE == kGateUp) {
+      const int tok = it.shared ? tt : uniform(cview<int32_t>(A.pairs)[it.src_base + tt]) / A.k;
+      rowp = A.x + static_cast<size_t>(tok) * C;
+    } else if constexpr (MODE == kDown) {
+      rowp = it.shared ? A.act_shared + static_cast<size_t>(tt) * C
+                       : A.act + static_cast<size_t>(it.src_base + tt) * C;
+    } else {
+      rowp = A.x + static_cast<size_t>(tt) * C;
+    }
+    S.xbase[t] = gview<u32x4>(rowp) + (lane & 15);
   }
+}
+
+template <int MODE, int Q, int NT>
+MOE_INLINE void run_group_streamed(const KArgs& A, const Item& it, Stream<Q, NT>& S, int g0, int ng) {
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+  stream_columns<Q, NT>(S, static_cast<uint32_t>(threadIdx.x & 63) * 4u, acc);
+  reduce_and_store<MODE, NT>(A, it, g0, ng, acc);
+}
+
+template <int MODE, int Q, int NT>
+MOE_INLINE void run_group(const KArgs& A, const Item& it, int g0, int ng) {
+  Stream<Q, NT> S;
+  make_stream<MODE, Q, NT>(A, it, g0, ng, S);
+  S.prologue();
+  run_group_streamed<MODE, Q, NT>(A, it, S, g0, ng);
 }
 
 MOE_INLINE bool block_ok(const moe_apq_block& b, int rows, int cols) {
@@ -339,10 +460,284 @@ MOE_INLINE bool block_ok(const moe_apq_block& b, int rows, int cols) {
          b.cols == cols && b.q >= 1 && b.q <= 8 && b.state == MOE_PAGE_GPU;
 }
 
+// Item i of the launch's list: shared-expert tiles first (they carry every token), then the
+// routed experts' tiles.  Returns false (and records the block) if its descriptor is invalid.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void apq_tile_kernel(KArgs A) {
+MOE_INLINE bool decode_item(const KArgs& A, int i, int sh_tiles, int tiles, Item& it) {
   constexpr int kTileRows = MODE == kGateUp ? kGateUpTileRows : kRowPanel;
-  // item list: shared-expert tiles first (they carry every token), then routed tiles
+  moe_apq_block b;
+  int inter = 0;
+  it.expert = -1;
+  if constexpr (MODE == kPlain) {
+    b = A.plain;
+    it.r0 = i * kRowPanel;
+    it.n = A.T;
+    it.src_base = 0;
+    it.shared = false;
+  } else {
+    if (i < sh_tiles) {
+      b = A.shared[MODE];
+      it.shared = true;
+      it.r0 = i * kTileRows;
+      it.n = A.T;
+      it.src_base = 0;
+      inter = A.I_shared;
+    } else {
+      const int a = (i - sh_tiles) / tiles, tile = (i - sh_tiles) - a * tiles;
+      it.expert = uniform(cview<int32_t>(A.active)[a]);
+      b = A.table[it.expert * 2 + MODE];
+      it.shared = false;
+      it.r0 = tile * kTileRows;
+      it.src_base = uniform(cview<int32_t>(A.offsets)[it.expert]);
+      it.n = uniform(cview<int32_t>(A.offsets)[it.expert + 1]) - it.src_base;
+      inter = A.I;
+    }
+    const int want_rows = MODE == kGateUp ? 2 * inter : A.H;
+    const int want_cols = MODE == kGateUp ? A.H : inter;
+    if (!block_ok(b, want_rows, want_cols)) return false;
+  }
+  it.row_hi = MODE == kGateUp ? inter + it.r0 : it.r0 + 32;
+  it.planes = b.planes;
+  it.lut = b.lut;
+  it.rows = b.rows;
+  it.cols = b.cols;
+  it.q = b.q;
+  return true;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Dense tiles (many tokens on one block: the shared expert, hot experts): matrix-core path.
+//
+// The weights are decoded exactly as above (one row per lane, 64 rows); the products go to
+// v_mfma_f32_32x32x16_f16.  Its A operand is a lane's 8 decoded weights of one 8-column octet,
+// so lanes 0-31 feed rows 0-31 as k 0-7 and lanes 32-63 feed rows 32-63 as k 8-15.  The B
+// operand separates the two row halves in the N dimension: column n < 16 carries token n on
+// k 0-7 (zero on k 8-15), column 16 + n carries token n on k 8-15 (zero on k 0-7).  One MFMA
+// per octet thus computes all 64 rows for 16 tokens: D[m][n] = row m . x_n and
+// D[m][16 + n] = row 32 + m . x_n.  B lanes that carry zeros use out-of-range buffer offsets,
+// which read as zero without touching memory.
+// ---------------------------------------------------------------------------------------------
+template <int Q>
+struct DenseStream {
+  static constexpr int D = 2;
+  u32x4 buf[D][Q];       // plane units of a chunk
+  u32x4 xw[2][4];        // B operand of a word (4 octets), double-buffered by word parity
+  const AS_GLOBAL u32x4* pbase;
+  size_t plane_u4;
+  __amdgpu_buffer_rsrc_t xrsrc;
+  uint32_t xoff;         // byte offset of this lane's token row (out of range: zero lane)
+  int cb, ce;
+
+  MOE_INLINE void issue_planes(int slot, int c) {
+#pragma unroll
+    for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u4 + static_cast<size_t>(c) * 64];
+  }
+  MOE_INLINE void issue_x(int wslot, int c, int jw) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      xw[wslot][b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   xrsrc, xoff + static_cast<uint32_t>(c * 256 + jw * 64 + b * 16), 0, 0));
+  }
+  MOE_INLINE void prologue() {
+#pragma unroll
+    for (int s = 0; s < D; ++s)
+      if (cb + s < ce) issue_planes(s, cb + s);
+    if (cb < ce) issue_x(0, cb, 0);
+  }
+};
+
+template <int Q, int JW>
+MOE_INLINE void dense_word(const DenseStream<Q>& S, int s, uint32_t lane4, f32x16& acc) {
+  uint32_t w[Q];
+#pragma unroll
+  for (int p = 0; p < Q; ++p) w[p] = word_of(S.buf[s][p], JW);
+  uint32_t wv[16];
+  decode_word<Q>(w, lane4, wv);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const u32x4 a = {wv[4 * b], wv[4 * b + 1], wv[4 * b + 2], wv[4 * b + 3]};  // columns 8b..8b+7
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                                  __builtin_bit_cast(half8_t, S.xw[JW & 1][b]),
+                                                  acc, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int Q, int JW>
+MOE_INLINE void dense_step(DenseStream<Q>& S, int s, int c, uint32_t lane4, f32x16& acc) {
+  // the next word's B operand is requested before this word is decoded
+  if constexpr (JW < 3) S.issue_x((JW + 1) & 1, c, JW + 1);
+  else if (c + 1 < S.ce) S.issue_x(0, c + 1, 0);
+  dense_word<Q, JW>(S, s, lane4, acc);
+}
+
+template <int Q>
+MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& acc) {
+  constexpr int D = DenseStream<Q>::D;
+  for (int c0 = S.cb; c0 < S.ce; c0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int c = c0 + s;
+      if (c < S.ce) {
+        dense_step<Q, 0>(S, s, c, lane4, acc);
+        dense_step<Q, 1>(S, s, c, lane4, acc);
+        dense_step<Q, 2>(S, s, c, lane4, acc);
+        dense_step<Q, 3>(S, s, c, lane4, acc);
+        if (c + D < S.ce) S.issue_planes(s, c + D);
+      }
+    }
+  }
+}
+
+// B-operand source of the tokens [g0, g0 + ng) for this lane: token n = lane (lanes 0-15) or
+// lane - 48 (lanes 48-63); every other lane reads zeros.
+template <int MODE, int Q>
+MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng, DenseStream<Q>& S) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int C = it.cols;
+  const int row = lane_row(it, lane);
+  const int nc4 = C / kColChunk;
+  S.pbase = gview<u32x4>(it.planes) + static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
+  S.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
+  S.cb = uniform((nc4 * wave) / kWavesPerTile);
+  S.ce = uniform((nc4 * (wave + 1)) / kWavesPerTile);
+  const int n = lane < 16 ? lane : lane - 48;
+  const bool real = (lane < 16 || lane >= 48) && n < ng;
+  const uint16_t* base;
+  size_t rows_total;
+  int row_index = 0;
+  if constexpr (MODE == kGateUp) {
+    base = A.x;
+    rows_total = A.T;
+    if (real) row_index = it.shared ? g0 + n : A.pairs[it.src_base + g0 + n] / A.k;
+  } else if constexpr (MODE == kDown) {
+    base = it.shared ? A.act_shared : A.act;
+    rows_total = it.shared ? static_cast<size_t>(A.T) : static_cast<size_t>(A.T) * A.k;
+    if (real) row_index = it.shared ? g0 + n : it.src_base + g0 + n;
+  } else {
+    base = A.x;
+    rows_total = A.T;
+    if (real) row_index = g0 + n;
+  }
+  const size_t bytes = rows_total * C * 2;
+  S.xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
+                                              static_cast<int>(bytes), 0x00020000);
+  S.xoff = real ? static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) : 0x80000000u;
+}
+
+// D layout of the 32x32 MFMA: lane l, register i holds D[m][l % 32] with
+// m = 8 (i / 4) + 4 (l / 32) + i % 4.  Column n < 16 is token n of rows m (tile rows 0-31);
+// column 16 + n is token n of rows 32 + m.
+template <int MODE>
+MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, f32x16& acc) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  float* red = reinterpret_cast<float*>(g_lds + kTblWords);
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[((wave - 1) * 16 + i) * 64 + lane] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+#pragma unroll
+      for (int w = 1; w < kWavesPerTile; ++w) acc[i] += red[((w - 1) * 16 + i) * 64 + lane];
+    }
+    const int col = lane & 31;
+    const int half = col >> 4, tok = col & 15;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const float v = acc[i];
+      if constexpr (MODE == kGateUp) {
+        const float up = __shfl_down(v, 16, 64);  // same m, row 32 + m, held 16 lanes up
+        if (half == 0 && tok < ng) {
+          const float a = v / (1.0f + expf(-v)) * up;  // SiLU(gate) * up
+          const int Iw = it.shared ? A.I_shared : A.I;
+          uint16_t* dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + tok) * Iw
+                                    : A.act + static_cast<size_t>(it.src_base + g0 + tok) * Iw;
+          dst[it.r0 + m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
+        }
+      } else if constexpr (MODE == kDown) {
+        if (tok < ng) {
+          const int r = it.r0 + 32 * half + m;
+          if (it.shared) {
+            const float s = A.shared_scale ? A.shared_scale[g0 + tok] : 1.0f;
+            A.part_shared[static_cast<size_t>(g0 + tok) * A.H + r] = s * v;
+          } else {
+            const int p = A.pairs[it.src_base + g0 + tok];
+            A.part[static_cast<size_t>(p) * A.H + r] = A.gates[p] * v;
+          }
+        }
+      } else {
+        if (tok < ng) A.y_plain[static_cast<size_t>(g0 + tok) * it.rows + it.r0 + 32 * half + m] = v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int MODE, int Q>
+MOE_INLINE void run_item_dense(const KArgs& A, const Item& it) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  u32x4 L[kLutRegs];
+  prefetch_lut(it, lane, wave, L);
+  DenseStream<Q> S;
+  make_dense_stream<MODE, Q>(A, it, 0, min(kDenseGroup, it.n), S);
+  S.prologue();
+  write_table<Q>(L, lane, wave);
+  __syncthreads();
+  for (int g0 = 0; g0 < it.n; g0 += kDenseGroup) {
+    const int ng = min(kDenseGroup, it.n - g0);
+    if (g0 > 0) {
+      make_dense_stream<MODE, Q>(A, it, g0, ng, S);
+      S.prologue();
+    }
+    f32x16 acc = {};
+    dense_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, acc);
+    dense_reduce_and_store<MODE>(A, it, g0, ng, acc);
+  }
+}
+
+// One row tile: the LUT rows and the first chunks of the first token group's stream (planes and
+// activations) are requested together, so their latencies overlap; the table is then written
+// from registers and the columns stream through.  (The second workgroup on the CU computes while
+// this one waits.)  Groups after the first (more than 4 tokens) take another pass.
+template <int MODE, int Q, int NT0>
+MOE_INLINE void run_item_first(const KArgs& A, const Item& it) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  u32x4 L[kLutRegs];
+  prefetch_lut(it, lane, wave, L);
+  const int ng0 = min(kMaxTokGroup, it.n);
+  Stream<Q, NT0> S;
+  make_stream<MODE, Q, NT0>(A, it, 0, ng0, S);
+  S.prologue();
+  write_table<Q>(L, lane, wave);
+  __syncthreads();
+  run_group_streamed<MODE, Q, NT0>(A, it, S, 0, ng0);
+  for (int g0 = kMaxTokGroup; g0 < it.n; g0 += kMaxTokGroup) {
+    const int ng = min(kMaxTokGroup, it.n - g0);
+    if (ng == 1) run_group<MODE, Q, 1>(A, it, g0, ng);
+    else if (ng == 2) run_group<MODE, Q, 2>(A, it, g0, ng);
+    else run_group<MODE, Q, 4>(A, it, g0, ng);
+  }
+}
+
+template <int MODE, int Q>
+MOE_INLINE void run_item(const KArgs& A, const Item& it) {
+  if (it.n >= A.dense_threshold) run_item_dense<MODE, Q>(A, it);
+  else if (it.n == 1) run_item_first<MODE, Q, 1>(A, it);
+  else if (it.n == 2) run_item_first<MODE, Q, 2>(A, it);
+  else run_item_first<MODE, Q, 4>(A, it);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
+  constexpr int kTileRows = MODE == kGateUp ? kGateUpTileRows : kRowPanel;
   int sh_tiles = 0, tiles = 0, n_routed = 0;
   if constexpr (MODE == kPlain) {
     tiles = A.plain.rows / kRowPanel;
@@ -355,49 +750,15 @@ __global__ __launch_bounds__(kThreads) void apq_tile_kernel(KArgs A) {
   const int total = sh_tiles + n_routed * tiles;
   for (int i = blockIdx.x; i < total; i += gridDim.x) {
     Item it;
-    moe_apq_block b;
-    int expert = -1, inter = 0;
-    if constexpr (MODE == kPlain) {
-      b = A.plain;
-      it.r0 = i * kRowPanel;
-      it.n = A.T;
-      it.src_base = 0;
-      it.shared = false;
-    } else if (i < sh_tiles) {
-      b = A.shared[MODE];
-      it.shared = true;
-      it.r0 = i * kTileRows;
-      it.n = A.T;
-      it.src_base = 0;
-      inter = A.I_shared;
-    } else {
-      const int a = (i - sh_tiles) / tiles, tile = (i - sh_tiles) - a * tiles;
-      expert = uniform(cview<int32_t>(A.active)[a]);
-      b = A.table[expert * 2 + MODE];
-      it.shared = false;
-      it.r0 = tile * kTileRows;
-      it.src_base = uniform(cview<int32_t>(A.offsets)[expert]);
-      it.n = uniform(cview<int32_t>(A.offsets)[expert + 1]) - it.src_base;
-      inter = A.I;
-    }
-    it.row_hi = MODE == kGateUp ? inter + it.r0 : it.r0 + 32;
-    if constexpr (MODE != kPlain) {
-      const int want_rows = MODE == kGateUp ? 2 * inter : A.H;
-      const int want_cols = MODE == kGateUp ? A.H : inter;
-      if (!block_ok(b, want_rows, want_cols)) {
-        if (threadIdx.x == 0) {
-          atomicOr(&A.err[0], 1);
-          A.err[1] = expert;
-          A.err[2] = MODE;
-        }
-        continue;
+    if (!decode_item<MODE>(A, i, sh_tiles, tiles, it)) {
+      if (threadIdx.x == 0) {
+        atomicOr(&A.err[0], 1);
+        A.err[1] = it.expert;
+        A.err[2] = MODE;
       }
+      continue;
     }
-    it.planes = b.planes;
-    it.lut = b.lut;
-    it.rows = b.rows;
-    it.cols = b.cols;
-    switch (b.q) {
+    switch (it.q) {
       case 1: run_item<MODE, 1>(A, it); break;
       case 2: run_item<MODE, 2>(A, it); break;
       case 3: run_item<MODE, 3>(A, it); break;

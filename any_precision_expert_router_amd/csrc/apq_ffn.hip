@@ -24,6 +24,7 @@ int launch_apq_ffn(const FfnArgs& a, hipStream_t stream) {
   k.act = a.ws.act; k.act_shared = a.ws.act_shared;
   k.part = a.ws.part; k.part_shared = a.ws.part_shared;
   k.err = a.ws.err;
+  k.dense_threshold = a.dense_threshold > 0 ? a.dense_threshold : kDefaultDenseThreshold;
   const int sh = a.shared ? 1 : 0;
   const int gu_items = sh * (a.I_shared / kGateUpTileRows) + a.E * (a.I / kGateUpTileRows);
   if (int rc = apq::launch_gate_up(k, gu_items, stream)) return rc;
@@ -33,12 +34,13 @@ int launch_apq_ffn(const FfnArgs& a, hipStream_t stream) {
 }
 
 int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y,
-                    hipStream_t stream) {
+                    int dense_threshold, hipStream_t stream) {
   apq::KArgs k{};
   k.plain = blk;
   k.T = T;
   k.x = x;
   k.y_plain = y;
+  k.dense_threshold = dense_threshold > 0 ? dense_threshold : kDefaultDenseThreshold;
   return apq::launch_plain(k, blk.rows / kRowPanel, stream);
 }
 

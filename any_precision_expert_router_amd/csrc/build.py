@@ -41,7 +41,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
-            cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", HERE, "-c", os.path.join(HERE, src), "-o", obj]
+            cmd = [hipcc(), *HIPCC_FLAGS, "-save-temps=obj", "-I", INCLUDE, "-I", HERE, "-c",
+                   os.path.join(HERE, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -49,6 +50,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 _wait(procs.pop(0))
         for p in procs:
             _wait(p)
+        _check_isa(tmp)
         tmp_out = os.path.join(tmp, LIB_NAME)
         link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_out, "-lpthread"]
         if verbose:
@@ -58,6 +60,21 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             raise RuntimeError("link failed:\n" + res.stdout.decode(errors="replace"))
         shutil.move(tmp_out, out)
     return out
+
+
+def _check_isa(tmp: str) -> None:
+    """Fail the build if the device assembly has a DPP wait-state hazard (see isa_check.py)."""
+    import glob
+    sys.path.insert(0, HERE)
+    import isa_check
+    total = 0
+    for path in sorted(glob.glob(os.path.join(tmp, f"*-hip-amdgcn-amd-amdhsa-{ARCH}.s"))):
+        n, problems = isa_check.check(path)
+        total += n
+        if problems:
+            raise RuntimeError(f"DPP hazards in {os.path.basename(path)}:\n" + "\n".join(problems[:20]))
+    if total == 0:
+        raise RuntimeError("no DPP instructions found in the device assembly: ISA check did not run")
 
 
 def _wait(item):

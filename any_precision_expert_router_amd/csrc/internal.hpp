@@ -71,10 +71,14 @@ struct FfnArgs {
   const float* shared_scale;
   uint16_t* y;
   Workspace ws;
+  int dense_threshold;  // <= 0: library default
 };
 int launch_apq_ffn(const FfnArgs& a, hipStream_t stream);
 int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y,
-                    hipStream_t stream);
+                    int dense_threshold, hipStream_t stream);
+
+// Tiles with at least this many tokens use the matrix-core (MFMA) path by default.
+constexpr int kDefaultDenseThreshold = 5;
 int launch_decode_indices(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
 
 }  // namespace moeapq

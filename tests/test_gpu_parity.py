@@ -137,10 +137,12 @@ def test_decode_indices_bit_exact(q):
     np.testing.assert_array_equal(out.cpu().numpy(), oracle.committed_index(idx8, q))
 
 
+@pytest.mark.parametrize("dense", [0, 1], ids=["auto", "mfma"])
 @pytest.mark.parametrize("q", range(1, 9))
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 16, 17, 40])
-def test_gemv_matches_oracle(q, T):
-    say(f"gemv q={q} T={T}")
+def test_gemv_matches_oracle(q, T, dense):
+    """Both product paths (packed-dot VALU below the dense threshold, MFMA at or above it)."""
+    say(f"gemv q={q} T={T} dense={dense}")
     R, C = 128, 640
     r = np.random.default_rng(q * 100 + T)
     idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
@@ -148,13 +150,14 @@ def test_gemv_matches_oracle(q, T):
     x = r.standard_normal((T, C)).astype(np.float16)
     blk, keep = _upload_block(idx8, q, lut)
     y = torch.empty((T, R), dtype=torch.float32, device=DEV)
-    apq.moe_apq_gemv(blk, _t(x), y)
+    apq.moe_apq_gemv(blk, _t(x), y, dense_threshold=1 if dense else 0)
     ref = oracle.apq_matvec(oracle.committed_index(idx8, q), lut, x.astype(np.float64).T).T
     assert oracle.rel_l2(y.cpu().numpy(), ref) <= 1e-5
 
 
+@pytest.mark.parametrize("dense", [1000, 1], ids=["valu", "mfma"])
 @pytest.mark.parametrize("q", range(1, 9))
-def test_gemv_one_hot_probe_is_exact_lut_read(q):
+def test_gemv_one_hot_probe_is_exact_lut_read(q, dense):
     """x = e_c gives y_r = LUT_r[idx_q(r, c)] exactly: pins the decode through the GEMV."""
     R, C = 64, 256
     r = np.random.default_rng(50 + q)
@@ -166,7 +169,7 @@ def test_gemv_one_hot_probe_is_exact_lut_read(q):
         x[t, c] = 1.0
     blk, keep = _upload_block(idx8, q, lut)
     y = torch.empty((len(cols), R), dtype=torch.float32, device=DEV)
-    apq.moe_apq_gemv(blk, _t(x), y)
+    apq.moe_apq_gemv(blk, _t(x), y, dense_threshold=dense)
     idx = oracle.committed_index(idx8, q)
     expect = np.stack([lut[np.arange(R), idx[:, c]].astype(np.float32) for c in cols])
     np.testing.assert_array_equal(y.cpu().numpy(), expect)
@@ -175,22 +178,23 @@ def test_gemv_one_hot_probe_is_exact_lut_read(q):
 # ------------------------------------------------------------------------------------------
 # the layer
 # ------------------------------------------------------------------------------------------
-def _run_layer(shape, inputs, dl, shared_scale=None):
+def _run_layer(shape, inputs, dl, shared_scale=None, threshold=0):
     T = shape.T
     y = torch.empty((T, shape.H), dtype=torch.float16, device=DEV)
     ws = torch.zeros(apq.moe_workspace_bytes(T, shape.E, shape.H, shape.I, shape.k, shape.I_shared),
                      dtype=torch.uint8, device=DEV)
     ss = None if shared_scale is None else _t(shared_scale.astype(np.float32))
     apq.moe_layer_forward(_t(inputs.logits), _t(inputs.x), shape.E, shape.H, shape.I, shape.k, dl.table,
-                          y, ws, shared=dl.shared, I_shared=shape.I_shared, shared_scale=ss)
+                          y, ws, shared=dl.shared, I_shared=shape.I_shared, shared_scale=ss,
+                          prefill_threshold=threshold)
     apq.moe_check_device_error(ws)
     return y.float().cpu().numpy().astype(np.float64), ws
 
 
-def _check_layer(shape, q_override=None, shared_scale=None, tokens=None, seed=0):
+def _check_layer(shape, q_override=None, shared_scale=None, tokens=None, seed=0, threshold=0):
     inputs = wl.gen_layer_inputs(shape, seed)
     dl = gpu_layers.device_layer(shape, q_override=q_override)
-    y, _ = _run_layer(shape, inputs, dl, shared_scale)
+    y, _ = _run_layer(shape, inputs, dl, shared_scale, threshold)
     get, sh = gpu_layers.oracle_getters(shape, q_override)
     ref = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh,
                                shared_scale=shared_scale, tokens=tokens)
@@ -205,16 +209,18 @@ def test_layer_tiny():
     _check_layer(wl.TINY)
 
 
-def test_layer_every_width_in_one_call_ragged_tokens():
+@pytest.mark.parametrize("threshold", [0, 1, 1000], ids=["auto", "all-mfma", "all-valu"])
+def test_layer_every_width_in_one_call_ragged_tokens(threshold):
     shape = wl.TINY.replace(H=256, E=12, I=384, k=3, T=21, name="mixed widths 1..8")
     q = np.array([[1 + (2 * e + m) % 8 for m in range(2)] for e in range(shape.E)], dtype=np.uint8)
-    _check_layer(shape, q_override=q)
+    _check_layer(shape, q_override=q, threshold=threshold)
 
 
-def test_layer_with_shared_expert_and_scale():
+@pytest.mark.parametrize("threshold", [0, 1, 1000], ids=["auto", "all-mfma", "all-valu"])
+def test_layer_with_shared_expert_and_scale(threshold):
     shape = wl.TINY.replace(H=256, E=8, I=256, k=2, T=19, I_shared=512, q_shared=8, name="shared")
     r = np.random.default_rng(3)
-    _check_layer(shape, shared_scale=r.uniform(-1, 2, size=shape.T))
+    _check_layer(shape, shared_scale=r.uniform(-1, 2, size=shape.T), threshold=threshold)
 
 
 def test_layer_k1_and_k_equals_E():
@@ -222,10 +228,11 @@ def test_layer_k1_and_k_equals_E():
     _check_layer(wl.TINY.replace(k=8, T=6, name="k=E"))
 
 
-def test_layer_many_tokens_on_one_expert():
-    """More than one 16-token group per expert (tokens beyond the group re-use the tile)."""
+@pytest.mark.parametrize("threshold", [0, 1000], ids=["auto", "all-valu"])
+def test_layer_many_tokens_on_one_expert(threshold):
+    """More tokens per expert than one pass takes (several 16-token MFMA or 4-token VALU passes)."""
     shape = wl.TINY.replace(E=4, k=2, T=70, name="hot experts")
-    _check_layer(shape)
+    _check_layer(shape, threshold=threshold)
 
 
 def test_layer_is_deterministic():
