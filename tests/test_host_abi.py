@@ -92,9 +92,9 @@ def test_argument_validation_happens_before_any_launch():
     blk = apq.ApqBlock(fake, fake, 64, 100, 4, 4, 0, 0, 0)
     assert lib.moe_apq_decode_indices(apq.ctypes.byref(blk), fake, None) == apq.MOE_EINVAL
     blk = apq.ApqBlock(fake, fake, 64, 128, 9, 4, 0, 0, 0)
-    assert lib.moe_apq_gemv(apq.ctypes.byref(blk), fake, 1, fake, None) == apq.MOE_EINVAL
+    assert lib.moe_apq_gemv(apq.ctypes.byref(blk), fake, 1, fake, 0, None) == apq.MOE_EINVAL
     blk = apq.ApqBlock(fake + 4, fake, 64, 128, 4, 4, 0, 0, 0)
-    assert lib.moe_apq_gemv(apq.ctypes.byref(blk), fake, 1, fake, None) == apq.MOE_EINVAL  # alignment
+    assert lib.moe_apq_gemv(apq.ctypes.byref(blk), fake, 1, fake, 0, None) == apq.MOE_EINVAL  # alignment
 
 
 def test_workspace_bytes_cover_the_sections():
