@@ -190,6 +190,28 @@ MOE_INLINE void prefetch_lut(const Item& it, int lane, int wave, u32x4 (&L)[kLut
   }
 }
 
+// The same, for an item whose width is known at compile time (only the registers it needs).
+template <int Q>
+MOE_INLINE void prefetch_lut_q(const Item& it, int lane, int wave, u32x4 (&L)[kLutRegs]) {
+  const AS_GLOBAL char* g = gview<char>(reinterpret_cast<const char*>(it.lut) +
+                                        static_cast<size_t>(lane_row(it, lane)) * (2u << Q));
+  if constexpr (Q == 1) {
+    L[0].x = *reinterpret_cast<const AS_GLOBAL uint32_t*>(g);
+  } else if constexpr (Q == 2) {
+    const uint64_t v = *reinterpret_cast<const AS_GLOBAL uint64_t*>(g);
+    L[0].x = static_cast<uint32_t>(v);
+    L[0].y = static_cast<uint32_t>(v >> 32);
+  } else if constexpr (Q <= 4) {
+#pragma unroll
+    for (int r = 0; r < (1 << (Q - 3)); ++r) L[r] = reinterpret_cast<const AS_GLOBAL u32x4*>(g)[r];
+  } else {
+    constexpr int n4 = 1 << (Q - 5);
+    const AS_GLOBAL u32x4* src = reinterpret_cast<const AS_GLOBAL u32x4*>(g) + wave * n4;
+#pragma unroll
+    for (int r = 0; r < n4; ++r) L[r] = src[r];
+  }
+}
+
 // fp16 number h (0-based) of the prefetched registers, as the byte pair a v_perm selects.
 MOE_INLINE uint32_t lut_dword(const u32x4 (&L)[kLutRegs], int h) { return word_of(L[h >> 3], (h >> 1) & 3); }
 
@@ -276,90 +298,6 @@ MOE_INLINE float dot2_bcast(float acc, uint32_t w, uint32_t x) {
   return acc;
 }
 
-// The wavefront's chunk stream: its column chunks [cb, ce) of the tile, with the q plane units
-// and the NT tokens' activation dwords of each chunk loaded D chunks ahead.  Planes and
-// activations share the in-order vector-memory counter, so waiting for one chunk never waits on
-// anything issued later.
-template <int Q, int NT>
-struct Stream {
-  static constexpr int D = ring_depth<Q>();
-  u32x4 buf[D][Q];
-  u32x4 xbuf[D][NT];
-  const AS_GLOBAL u32x4* pbase;       // this lane's unit of plane 0, chunk 0
-  const AS_GLOBAL u32x4* xbase[NT];   // token t's row + this lane's 16 bytes of chunk 0
-  size_t plane_u4;
-  int cb, ce;
-
-  MOE_INLINE void issue(int slot, int c) {
-#pragma unroll
-    for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u4 + static_cast<size_t>(c) * 64];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) xbuf[slot][t] = xbase[t][static_cast<size_t>(c) * 16];
-  }
-  MOE_INLINE void prologue() {
-#pragma unroll
-    for (int s = 0; s < D; ++s)
-      if (cb + s < ce) issue(s, cb + s);
-  }
-};
-
-template <int Q, int NT, int JW>
-MOE_INLINE void word_products(const Stream<Q, NT>& S, int s, const uint32_t (&wv)[16], float (&acc)[NT]) {
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const u32x4& xv = S.xbuf[s][t];
-    // dword d of word JW is dword 16*JW + d of the chunk: lane 4*JW + d/4, component d%4
-    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[0], xv.x);
-    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[1], xv.y);
-    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[2], xv.z);
-    acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[3], xv.w);
-    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[4], xv.x);
-    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[5], xv.y);
-    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[6], xv.z);
-    acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[7], xv.w);
-    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[8], xv.x);
-    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[9], xv.y);
-    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[10], xv.z);
-    acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[11], xv.w);
-    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[12], xv.x);
-    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[13], xv.y);
-    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[14], xv.z);
-    acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[15], xv.w);
-  }
-}
-
-template <int Q, int NT, int JW>
-MOE_INLINE void one_word(const Stream<Q, NT>& S, int s, uint32_t lane4, float (&acc)[NT]) {
-  uint32_t w[Q];
-#pragma unroll
-  for (int p = 0; p < Q; ++p) w[p] = word_of(S.buf[s][p], JW);
-  uint32_t wv[16];
-  decode_word<Q>(w, lane4, wv);
-  word_products<Q, NT, JW>(S, s, wv, acc);
-  // keep the next word's lookups below this word's products: bounds live registers
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// acc[t] += sum over the stream's columns of W[row(lane), c] x_t[c]; consumes the ring that
-// prologue() filled and refills each slot D chunks ahead once its chunk is decoded.
-template <int Q, int NT>
-MOE_INLINE void stream_columns(Stream<Q, NT>& S, uint32_t lane4, float (&acc)[NT]) {
-  constexpr int D = Stream<Q, NT>::D;
-  for (int c0 = S.cb; c0 < S.ce; c0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const int c = c0 + s;
-      if (c < S.ce) {
-        one_word<Q, NT, 0>(S, s, lane4, acc);
-        one_word<Q, NT, 1>(S, s, lane4, acc);
-        one_word<Q, NT, 2>(S, s, lane4, acc);
-        one_word<Q, NT, 3>(S, s, lane4, acc);
-        if (c + D < S.ce) S.issue(s, c + D);
-      }
-    }
-  }
-}
-
 // Reduce the four wavefronts' partial sums (fixed order: wave 0 + 1 + 2 + 3) and apply the
 // epilogue of the mode for the ng real tokens of the group starting at g0.
 template <int MODE, int NT>
@@ -406,52 +344,6 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
     }
   }
   __syncthreads();
-}
-
-// The chunk stream of token group [g0, g0 + ng) for this wavefront (prologue not yet issued).
-template <int MODE, int Q, int NT>
-MOE_INLINE void make_stream(const KArgs& A, const Item& it, int g0, int ng, Stream<Q, NT>& S) {
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  const int C = it.cols;
-  const int row = lane_row(it, lane);
-  const int nc4 = C / kColChunk;
-  S.pbase = gview<u32x4>(it.planes) + static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
-  S.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
-  S.cb = uniform((nc4 * wave) / kWavesPerTile);
-  S.ce = uniform((nc4 * (wave + 1)) / kWavesPerTile);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int tt = g0 + (t < ng ? t : 0);  // padding slots repeat slot 0
-    const uint16_t* rowp;
-    if constexpr (MODE == kGateUp) {
-      const int tok = it.shared ? tt : uniform(cview<int32_t>(A.pairs)[it.src_base + tt]) / A.k;
-      rowp = A.x + static_cast<size_t>(tok) * C;
-    } else if constexpr (MODE == kDown) {
-      rowp = it.shared ? A.act_shared + static_cast<size_t>(tt) * C
-                       : A.act + static_cast<size_t>(it.src_base + tt) * C;
-    } else {
-      rowp = A.x + static_cast<size_t>(tt) * C;
-    }
-    S.xbase[t] = gview<u32x4>(rowp) + (lane & 15);
-  }
-}
-
-template <int MODE, int Q, int NT>
-MOE_INLINE void run_group_streamed(const KArgs& A, const Item& it, Stream<Q, NT>& S, int g0, int ng) {
-  float acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-  stream_columns<Q, NT>(S, static_cast<uint32_t>(threadIdx.x & 63) * 4u, acc);
-  reduce_and_store<MODE, NT>(A, it, g0, ng, acc);
-}
-
-template <int MODE, int Q, int NT>
-MOE_INLINE void run_group(const KArgs& A, const Item& it, int g0, int ng) {
-  Stream<Q, NT> S;
-  make_stream<MODE, Q, NT>(A, it, g0, ng, S);
-  S.prologue();
-  run_group_streamed<MODE, Q, NT>(A, it, S, g0, ng);
 }
 
 MOE_INLINE bool block_ok(const moe_apq_block& b, int rows, int cols) {
@@ -538,11 +430,13 @@ struct DenseStream {
       xw[wslot][b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                    xrsrc, xoff + static_cast<uint32_t>(c * 256 + jw * 64 + b * 16), 0, 0));
   }
+  // Loads are issued unconditionally (a chunk past the end re-reads the last one, a cache hit)
+  // so that the number of loads in flight never depends on run-time branches.
+  MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
   MOE_INLINE void prologue() {
 #pragma unroll
-    for (int s = 0; s < D; ++s)
-      if (cb + s < ce) issue_planes(s, cb + s);
-    if (cb < ce) issue_x(0, cb, 0);
+    for (int s = 0; s < D; ++s) issue_planes(s, clamp(cb + s));
+    issue_x(0, clamp(cb), 0);
   }
 };
 
@@ -567,7 +461,7 @@ template <int Q, int JW>
 MOE_INLINE void dense_step(DenseStream<Q>& S, int s, int c, uint32_t lane4, f32x16& acc) {
   // the next word's B operand is requested before this word is decoded
   if constexpr (JW < 3) S.issue_x((JW + 1) & 1, c, JW + 1);
-  else if (c + 1 < S.ce) S.issue_x(0, c + 1, 0);
+  else S.issue_x(0, S.clamp(c + 1), 0);
   dense_word<Q, JW>(S, s, lane4, acc);
 }
 
@@ -583,7 +477,7 @@ MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& acc) {
         dense_step<Q, 1>(S, s, c, lane4, acc);
         dense_step<Q, 2>(S, s, c, lane4, acc);
         dense_step<Q, 3>(S, s, c, lane4, acc);
-        if (c + D < S.ce) S.issue_planes(s, c + D);
+        S.issue_planes(s, S.clamp(c + D));
       }
     }
   }
@@ -702,37 +596,196 @@ MOE_INLINE void run_item_dense(const KArgs& A, const Item& it) {
   }
 }
 
-// One row tile: the LUT rows and the first chunks of the first token group's stream (planes and
-// activations) are requested together, so their latencies overlap; the table is then written
-// from registers and the columns stream through.  (The second workgroup on the CU computes while
-// this one waits.)  Groups after the first (more than 4 tokens) take another pass.
-template <int MODE, int Q, int NT0>
-MOE_INLINE void run_item_first(const KArgs& A, const Item& it) {
+// A tile that does not stream (at least as many tokens as the dense threshold, or more than 4):
+// matrix-core path.
+template <int MODE, int Q>
+MOE_INLINE void run_item(const KArgs& A, const Item& it) {
+  run_item_dense<MODE, Q>(A, it);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Streaming across items (VALU tiles with at most 4 tokens).  Each wavefront keeps one ring of
+// in-flight chunks (planes + the tokens' activations) running across consecutive items of the
+// same width: while item i computes, the ring slots it frees are refilled with item i+1's
+// first chunks and item i+1's LUT rows are fetched into registers, so HBM stays busy through
+// every tile boundary instead of alternating between a load burst and an idle compute phase.
+// ---------------------------------------------------------------------------------------------
+
+// One item's share of the columns for this wavefront.
+struct Geo {
+  const AS_GLOBAL u32x4* pbase;
+  const AS_GLOBAL u32x4* xbase[kMaxTokGroup];
+  size_t plane_u4;
+  int cb, n;  // first chunk and chunk count of this wavefront
+  int ng;     // tokens (1..4)
+};
+
+template <int MODE>
+MOE_INLINE void make_geo(const KArgs& A, const Item& it, Geo& G) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  u32x4 L[kLutRegs];
-  prefetch_lut(it, lane, wave, L);
-  const int ng0 = min(kMaxTokGroup, it.n);
-  Stream<Q, NT0> S;
-  make_stream<MODE, Q, NT0>(A, it, 0, ng0, S);
-  S.prologue();
-  write_table<Q>(L, lane, wave);
-  __syncthreads();
-  run_group_streamed<MODE, Q, NT0>(A, it, S, 0, ng0);
-  for (int g0 = kMaxTokGroup; g0 < it.n; g0 += kMaxTokGroup) {
-    const int ng = min(kMaxTokGroup, it.n - g0);
-    if (ng == 1) run_group<MODE, Q, 1>(A, it, g0, ng);
-    else if (ng == 2) run_group<MODE, Q, 2>(A, it, g0, ng);
-    else run_group<MODE, Q, 4>(A, it, g0, ng);
+  const int C = it.cols;
+  const int row = lane_row(it, lane);
+  const int nc4 = C / kColChunk;
+  G.pbase = gview<u32x4>(it.planes) + static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
+  G.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
+  G.cb = uniform((nc4 * wave) / kWavesPerTile);
+  G.n = uniform((nc4 * (wave + 1)) / kWavesPerTile) - G.cb;
+  G.ng = it.n;
+#pragma unroll
+  for (int t = 0; t < kMaxTokGroup; ++t) {
+    const int tt = t < it.n ? t : 0;  // unused slots repeat slot 0 (never loaded)
+    const uint16_t* rowp;
+    if constexpr (MODE == kGateUp) {
+      const int tok = it.shared ? tt : uniform(cview<int32_t>(A.pairs)[it.src_base + tt]) / A.k;
+      rowp = A.x + static_cast<size_t>(tok) * C;
+    } else if constexpr (MODE == kDown) {
+      rowp = it.shared ? A.act_shared + static_cast<size_t>(tt) * C
+                       : A.act + static_cast<size_t>(it.src_base + tt) * C;
+    } else {
+      rowp = A.x + static_cast<size_t>(tt) * C;
+    }
+    G.xbase[t] = gview<u32x4>(rowp) + (lane & 15);
   }
 }
 
+template <int Q>
+struct Ring {
+  static constexpr int D = ring_depth<Q>();
+  u32x4 buf[D][Q];
+  u32x4 xbuf[D][kMaxTokGroup];
+
+  // Chunk k (0-based within the wavefront's share) of geometry g into `slot` (compile-time).
+  // Every call issues exactly Q + 4 loads: unused token slots re-read token 0's activations, so
+  // the number of loads in flight never depends on run-time branches and the compiler's
+  // wait counts stay exact.
+  MOE_INLINE void issue(int slot, const Geo& g, int k) {
+    const size_t c = static_cast<size_t>(g.cb + k);
+#pragma unroll
+    for (int p = 0; p < Q; ++p) buf[slot][p] = g.pbase[p * g.plane_u4 + c * 64];
+#pragma unroll
+    for (int t = 0; t < kMaxTokGroup; ++t) xbuf[slot][t] = g.xbase[t][c * 16];
+  }
+};
+
+// Branch-free choice of the chunk a freed slot takes next: chunk w of the current item, else
+// chunk w - m of the next item, else (nothing left) a re-read of the chunk just consumed, which
+// hits in cache.
+MOE_INLINE void pick_refill(const Geo& cur, const Geo& nxt, bool cont, int v, int w, int m, Geo& g,
+                            int& k) {
+  const bool use_cur = w < cur.n;
+  const bool use_nxt = !use_cur && cont && w >= m && (w - m) < nxt.n;
+  g.pbase = use_nxt ? nxt.pbase : cur.pbase;
+  g.plane_u4 = use_nxt ? nxt.plane_u4 : cur.plane_u4;
+  g.cb = use_nxt ? nxt.cb : cur.cb;
+#pragma unroll
+  for (int t = 0; t < kMaxTokGroup; ++t) g.xbase[t] = use_nxt ? nxt.xbase[t] : cur.xbase[t];
+  k = use_cur ? w : (use_nxt ? w - m : (v < cur.n ? v : 0));
+}
+
+// Products of one 32-column word for the ng (<= 4) tokens of the ring slot.
+template <int Q, int JW>
+MOE_INLINE void ring_word(const Ring<Q>& R, int s, int ng, uint32_t lane4, float (&acc)[kMaxTokGroup]) {
+  uint32_t w[Q];
+#pragma unroll
+  for (int p = 0; p < Q; ++p) w[p] = word_of(R.buf[s][p], JW);
+  uint32_t wv[16];
+  decode_word<Q>(w, lane4, wv);
+#pragma unroll
+  for (int t = 0; t < kMaxTokGroup; ++t) {
+    if (t < ng) {
+      const u32x4& xv = R.xbuf[s][t];
+      // dword d of word JW is dword 16*JW + d of the chunk: lane 4*JW + d/4, component d%4
+      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[0], xv.x);
+      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[1], xv.y);
+      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[2], xv.z);
+      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[3], xv.w);
+      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[4], xv.x);
+      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[5], xv.y);
+      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[6], xv.z);
+      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[7], xv.w);
+      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[8], xv.x);
+      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[9], xv.y);
+      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[10], xv.z);
+      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[11], xv.w);
+      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[12], xv.x);
+      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[13], xv.y);
+      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[14], xv.z);
+      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[15], xv.w);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MODE>
+MOE_INLINE bool streamable(const KArgs& A, const Item& it) {
+  return it.n <= kMaxTokGroup && it.n < A.dense_threshold;
+}
+
+// Next valid item of this workgroup after item index i (reports invalid descriptors).
+template <int MODE>
+MOE_INLINE int next_item(const KArgs& A, int i, int total, int sh_tiles, int tiles, Item& nx) {
+  int j = i + gridDim.x;
+  while (j < total && !decode_item<MODE>(A, j, sh_tiles, tiles, nx)) {
+    if (threadIdx.x == 0) {
+      atomicOr(&A.err[0], 1);
+      A.err[1] = nx.expert;
+      A.err[2] = MODE;
+    }
+    j += gridDim.x;
+  }
+  return j;
+}
+
+// Process item `it` (index i) and every following item of the same width that is streamable.
+// On return, (i, it) is the first item not processed (i >= total when the list is exhausted).
 template <int MODE, int Q>
-MOE_INLINE void run_item(const KArgs& A, const Item& it) {
-  if (it.n >= A.dense_threshold) run_item_dense<MODE, Q>(A, it);
-  else if (it.n == 1) run_item_first<MODE, Q, 1>(A, it);
-  else if (it.n == 2) run_item_first<MODE, Q, 2>(A, it);
-  else run_item_first<MODE, Q, 4>(A, it);
+MOE_INLINE void valu_stream(const KArgs& A, int& i, Item& it, int total, int sh_tiles, int tiles) {
+  constexpr int D = Ring<Q>::D;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;
+  Ring<Q> R;
+  Geo cur, nxt;
+  u32x4 L[kLutRegs];
+  prefetch_lut_q<Q>(it, lane, wave, L);
+  make_geo<MODE>(A, it, cur);
+#pragma unroll
+  for (int s = 0; s < D; ++s) R.issue(s, cur, s < cur.n ? s : 0);
+  while (true) {
+    Item next;
+    const int j = next_item<MODE>(A, i, total, sh_tiles, tiles, next);
+    const bool cont = j < total && next.q == Q && streamable<MODE>(A, next);
+    if (cont) make_geo<MODE>(A, next, nxt);
+    write_table<Q>(L, lane, wave);
+    __syncthreads();
+    if (cont) prefetch_lut_q<Q>(next, lane, wave, L);
+    float acc[kMaxTokGroup] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // the wavefront walks its chunks padded to a multiple of D, so the next item's chunk k
+    // always lands in slot k % D
+    const int m = (cur.n + D - 1) / D * D;
+    for (int v0 = 0; v0 < m; v0 += D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        const int v = v0 + s;
+        if (v < cur.n) {
+          ring_word<Q, 0>(R, s, cur.ng, lane4, acc);
+          ring_word<Q, 1>(R, s, cur.ng, lane4, acc);
+          ring_word<Q, 2>(R, s, cur.ng, lane4, acc);
+          ring_word<Q, 3>(R, s, cur.ng, lane4, acc);
+        }
+        Geo g;
+        int k;
+        pick_refill(cur, nxt, cont, v, v + D, m, g, k);
+        R.issue(s, g, k);
+      }
+    }
+    reduce_and_store<MODE, kMaxTokGroup>(A, it, 0, it.n, acc);
+    i = j;
+    it = next;
+    if (!cont) return;
+    cur = nxt;
+  }
 }
 
 template <int MODE>
@@ -748,25 +801,33 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
     n_routed = uniform(cview<int32_t>(A.n_active)[0]);
   }
   const int total = sh_tiles + n_routed * tiles;
-  for (int i = blockIdx.x; i < total; i += gridDim.x) {
-    Item it;
-    if (!decode_item<MODE>(A, i, sh_tiles, tiles, it)) {
-      if (threadIdx.x == 0) {
-        atomicOr(&A.err[0], 1);
-        A.err[1] = it.expert;
-        A.err[2] = MODE;
+  Item it;
+  int i = next_item<MODE>(A, static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x), total,
+                          sh_tiles, tiles, it);
+  while (i < total) {
+    if (streamable<MODE>(A, it)) {
+      switch (it.q) {
+        case 1: valu_stream<MODE, 1>(A, i, it, total, sh_tiles, tiles); break;
+        case 2: valu_stream<MODE, 2>(A, i, it, total, sh_tiles, tiles); break;
+        case 3: valu_stream<MODE, 3>(A, i, it, total, sh_tiles, tiles); break;
+        case 4: valu_stream<MODE, 4>(A, i, it, total, sh_tiles, tiles); break;
+        case 5: valu_stream<MODE, 5>(A, i, it, total, sh_tiles, tiles); break;
+        case 6: valu_stream<MODE, 6>(A, i, it, total, sh_tiles, tiles); break;
+        case 7: valu_stream<MODE, 7>(A, i, it, total, sh_tiles, tiles); break;
+        default: valu_stream<MODE, 8>(A, i, it, total, sh_tiles, tiles); break;
       }
-      continue;
-    }
-    switch (it.q) {
-      case 1: run_item<MODE, 1>(A, it); break;
-      case 2: run_item<MODE, 2>(A, it); break;
-      case 3: run_item<MODE, 3>(A, it); break;
-      case 4: run_item<MODE, 4>(A, it); break;
-      case 5: run_item<MODE, 5>(A, it); break;
-      case 6: run_item<MODE, 6>(A, it); break;
-      case 7: run_item<MODE, 7>(A, it); break;
-      default: run_item<MODE, 8>(A, it); break;
+    } else {
+      switch (it.q) {
+        case 1: run_item<MODE, 1>(A, it); break;
+        case 2: run_item<MODE, 2>(A, it); break;
+        case 3: run_item<MODE, 3>(A, it); break;
+        case 4: run_item<MODE, 4>(A, it); break;
+        case 5: run_item<MODE, 5>(A, it); break;
+        case 6: run_item<MODE, 6>(A, it); break;
+        case 7: run_item<MODE, 7>(A, it); break;
+        default: run_item<MODE, 8>(A, it); break;
+      }
+      i = next_item<MODE>(A, i, total, sh_tiles, tiles, it);
     }
   }
 }

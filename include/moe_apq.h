@@ -128,10 +128,10 @@ int moe_group_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t* e
  *   topk_gates   fp32 [T][k] from moe_route_topk.
  *   shared       device moe_apq_block [2] (gate_up [2*I_shared x H], down [H x I_shared]) or
  *                NULL (then I_shared is ignored); shared_scale fp32 [T] or NULL (= 1).
- *   prefill_threshold: tiles of experts with at least this many routed pairs (and the shared
- *                expert's tiles when T reaches it) use the matrix-core (MFMA) product path, the
- *                others the packed-dot VALU path (<= 0: library default, 5).  Results agree up
- *                to fp32 summation order.
+ *   prefill_threshold: tiles of experts with at least min(prefill_threshold, 5) routed pairs (and
+ *                the shared expert's tiles when T reaches it) use the matrix-core (MFMA) product
+ *                path, the others the packed-dot VALU path (<= 0: library default, 5).  Results
+ *                agree up to fp32 summation order.
  *   y            out fp16 [T][H].
  *   workspace    >= moe_workspace_bytes(T, E, H, I, k, I_shared) bytes, 256-byte aligned.
  *   Device checks: a routed block whose descriptor does not match (rows, cols) of its module, has
@@ -172,8 +172,8 @@ int moe_apq_pack(const uint8_t* idx8_host, int rows, int cols, int q, uint32_t* 
  *   lookups moe_apq_ffn uses, in its plain mode).
  *   blk_host  host pointer to the descriptor (planes/lut are device pointers, 16-byte aligned).
  *   x         fp16 [T][cols];  y out fp32 [T][rows].
- *   dense_threshold: T at or above which the tile takes the matrix-core path (<= 0: default), so
- *             that both product paths can be checked on the same block.
+ *   dense_threshold: the tile takes the matrix-core path when T >= min(dense_threshold, 5)
+ *             (<= 0: default 5), so that both product paths can be checked on the same block.
  */
 int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float* y,
                  int dense_threshold, void* stream);
