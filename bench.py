@@ -1,0 +1,287 @@
+"""Benchmark of the decode-time Any-Precision MoE layer on one MI355X.
+
+One step = one moe_layer_forward call (route + group + gate_up/SiLU + down + combine) over a
+synthetic batch already resident in HBM.  The default workload is a Qwen1.5-MoE-A2.7B-shaped
+layer: H 2048, 60 routed experts of intermediate 1408 at 4 bits, top-4, plus one shared expert of
+intermediate 5632 at 8 bits, 16 decode tokens.  Weight copies are rotated so that the timed
+steps cannot be served from the 256-MB last-level cache.
+
+Prints one JSON line: value = effective weight GB/s (algorithmic plane + LUT bytes of the blocks
+one call reads, divided by the time per call), plus the roofline of the dominant kernel (event
+times on the launch stream) and the CPU oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+import workloads as wl  # noqa: E402
+
+METRIC = "µs per MoE decode layer + effective weight GB/s (% of MI355X HBM peak)"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+WORKLOADS = {
+    "qwen15_moe_a27b": wl.QWEN15_MOE_A27B,
+    "mixtral_8x7b": wl.MIXTRAL_8X7B,
+    "qwen3_next_80b_a3b": wl.QWEN3_NEXT_80B_A3B,
+    "qwen2_57b_a14b_t1": wl.QWEN2_57B_A14B.with_tokens(1),
+    "qwen2_57b_a14b_t8": wl.QWEN2_57B_A14B.with_tokens(8),
+    "qwen2_57b_a14b_t32": wl.QWEN2_57B_A14B.with_tokens(32),
+    "qwen2_57b_a14b_t128": wl.QWEN2_57B_A14B.with_tokens(128),
+    "tiny": wl.TINY,
+}
+# the FFN kernel whose roofline the line reports, and the blocks (module) it reads
+DOMINANT = {"kernel": "apq_gate_up_silu", "module": wl.GATE_UP}
+ENGINE_SOURCES = ["any_precision_expert_router_amd/csrc/apq_engine.hpp",
+                  "any_precision_expert_router_amd/csrc/apq_gate_up.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def engine_sha() -> str:
+    h = hashlib.sha256()
+    for rel in ENGINE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def module_bytes(shape, ids, module, widths):
+    """(planes, LUT) bytes of one module over the active experts (+ shared)."""
+    planes = lut = 0
+    for e in np.unique(ids):
+        r, c = wl.block_dims(shape, module, int(e))
+        p, l = wl.algorithmic_weight_bytes(r, c, int(widths[e, module]))
+        planes, lut = planes + p, lut + l
+    if shape.I_shared:
+        r, c = wl.block_dims(shape, module, wl.SHARED_EXPERT)
+        p, l = wl.algorithmic_weight_bytes(r, c, shape.q_shared)
+        planes, lut = planes + p, lut + l
+    return planes, lut
+
+
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel is unchanged."""
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("engine_sha") != engine_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, inputs, budget_s: float):
+    """The float64 oracle on the host cores: one whole layer call (all tokens), median of runs."""
+    import oracle
+    import gpu_layers
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    get, sh = gpu_layers.oracle_getters(shape, cache_size=2 * shape.E)
+    # draw the blocks first: generating inputs is not the oracle's work
+    ids, _ = oracle.route_topk(inputs.logits, shape.k)
+    for e in np.unique(ids):
+        get(int(e), 0), get(int(e), 1)
+    if sh:
+        sh(0, 0), sh(0, 1)
+    times = []
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        t_end = time.perf_counter() + budget_s
+        while len(times) < 3 and (not times or time.perf_counter() + times[-1] < t_end):
+            t0 = time.perf_counter()
+            oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh)
+            times.append(time.perf_counter() - t0)
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return statistics.median(times), len(times)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen15_moe_a27b", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies-gb", type=float, default=1.2,
+                    help="total bytes of rotated weight copies (defeats the last-level cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0)
+    ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one device copy of this many MiB: the known-size "
+                         "dispatch that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the layer is measured on "
+                          "one MI355X's share; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import any_precision_expert_router_amd as apq
+    import gpu_layers
+    import oracle
+
+    shape = WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {shape.name}, T={shape.T}: building weights")
+    inputs = wl.gen_layer_inputs(shape)
+    widths = wl.gen_widths(shape)
+    base = gpu_layers.device_layer(shape, device=dev)
+    copies = [base]
+    n_copies = max(1, int(np.ceil(args.copies_gb * 1e9 / base.weight_bytes)))
+    for _ in range(n_copies - 1):   # same bytes at other addresses
+        c = object.__new__(apq.DeviceLayer)
+        c.__dict__.update(base.__dict__)
+        c.arena = base.arena.clone()
+        delta = c.arena.data_ptr() - base.arena.data_ptr()
+        tbl = base.table.view(torch.int64).reshape(-1, 4).clone()
+        tbl[:, 0] += delta
+        tbl[:, 1] += delta
+        c.table = tbl.view(torch.uint8).reshape(-1)
+        if base.shared is not None:
+            sht = base.shared.view(torch.int64).reshape(-1, 4).clone()
+            sht[:, 0] += delta
+            sht[:, 1] += delta
+            c.shared = sht.view(torch.uint8).reshape(-1)
+        copies.append(c)
+    log(f"[bench] {n_copies} weight copies x {base.weight_bytes / 1e6:.1f} MB")
+
+    T = shape.T
+    logits = torch.from_numpy(inputs.logits).to(dev)
+    x = torch.from_numpy(inputs.x).to(dev)
+    y = torch.empty((T, shape.H), dtype=torch.float16, device=dev)
+    ws = torch.zeros(apq.moe_workspace_bytes(T, shape.E, shape.H, shape.I, shape.k, shape.I_shared),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = copies[i % len(copies)]
+        apq.moe_layer_forward(logits, x, shape.E, shape.H, shape.I, shape.k, c.table, y, ws,
+                              shared=c.shared, I_shared=shape.I_shared, stream=stream)
+
+    ids_ref, _ = oracle.route_topk(inputs.logits, shape.k)
+    planes_b, lut_b = gpu_layers.active_weight_bytes(shape, ids_ref, widths)
+    weight_bytes = planes_b + lut_b
+
+    # correctness of the timed configuration on the sampled tokens
+    if not args.no_check:
+        step(0)
+        apq.moe_check_device_error(ws)
+        get, sh = gpu_layers.oracle_getters(shape, cache_size=16)
+        tok = [0, T - 1] if T > 1 else [0]
+        ref = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh, tokens=tok)
+        yc = y.float().cpu().numpy()
+        errs = [oracle.rel_l2(yc[t], ref["y"][t]) for t in tok]
+        log(f"[bench] parity on tokens {tok}: rel L2 {['%.2e' % e for e in errs]}")
+        assert max(errs) <= 1e-3, errs
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_ms / args.steps
+    log(f"[bench] {args.steps} steps: wall {wall_ms:.2f} ms, events {ev_ms:.2f} ms "
+        f"-> {1e3 * ms_per_step:.2f} us/layer (events {1e3 * ev_ms / args.steps:.2f})")
+
+    # per-kernel durations: the same steps again with every library launch bracketed by events
+    apq.moe_profile_start()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = apq.moe_profile_stop()
+    per_kernel = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in prof.items()}
+    log("[bench] per-kernel (events): " + ", ".join(f"{k} {v['avg_us']:.2f} us" for k, v in per_kernel.items()))
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18   # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB read + {args.copy_probe_mib} MiB written")
+        del src, dst
+
+    dk = DOMINANT["kernel"]
+    dp, dl = module_bytes(shape, ids_ref, DOMINANT["module"], widths)
+    dom_us = per_kernel[dk]["avg_us"]
+    achieved = (dp + dl) / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dk, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(args.workload, dk),
+                "algorithmic_bytes_per_launch": int(dp + dl), "avg_launch_us": round(dom_us, 3)}
+
+    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_layer": round(1e3 * ms_per_step, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "experts": shape.E,
+                   "intermediate": shape.I, "top_k": shape.k, "shared_intermediate": shape.I_shared,
+                   "widths": sorted(set(int(v) for v in np.unique(widths))),
+                   "active_experts": int(len(np.unique(ids_ref))),
+                   "weight_bytes_per_call": int(weight_bytes), "plane_bytes": int(planes_b),
+                   "lut_bytes": int(lut_b), "weight_copies": n_copies},
+        "per_kernel_us": {k: round(v["avg_us"], 3) for k, v in per_kernel.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        med_s, runs = cpu_baseline(shape, inputs, args.cpu_budget_s)
+        out["cpu_baseline"] = {
+            "value": round(weight_bytes / med_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"one whole layer call ({T} tokens, float64 NumPy, BLAS limited to 1 thread), "
+                      f"median of {runs} runs: {1e3 * med_s:.0f} ms per layer",
+            "ms_per_layer": round(1e3 * med_s, 1),
+            "host_cores_available": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
