@@ -104,11 +104,6 @@ MOE_INLINE uint32_t lds_load(uint32_t byte_addr) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(g_lds) + byte_addr);
 }
 
-MOE_INLINE float dot2(uint32_t w, uint32_t x, float acc) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w), __builtin_bit_cast(half2_t, x),
-                                acc, false);
-}
-
 MOE_INLINE int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 MOE_INLINE uint32_t word_of(const u32x4& v, int jw) {
@@ -130,6 +125,8 @@ struct Item {
   int n;         // tokens routed to the tile
   int src_base;  // sorted position of the expert's first pair (routed), 0 (shared/plain)
   int expert;    // routed expert id, -1 for the shared expert / plain block
+  int c0, nc;    // the item's column chunks [c0, c0 + nc) (a segment of a long down row)
+  int seg;       // segment index (selects the partial-sum buffer of a down item)
   bool shared;
 };
 
@@ -152,6 +149,7 @@ struct KArgs {
   float* y_plain;               // fp32 [T][rows]
   int32_t* err;
   int dense_threshold;          // tiles with at least this many tokens take the MFMA path
+  int segs, segs_shared;        // column segments per down row tile (routed, shared expert)
 };
 
 MOE_INLINE int lane_row(const Item& it, int lane) {
@@ -286,16 +284,43 @@ MOE_INLINE void decode_word(const uint32_t (&w)[Q], uint32_t lane4, uint32_t (&w
   }
 }
 
-// acc += dot(w, x) with x broadcast from lane N of each 16-lane row (DPP row_newbcast): every
-// lane of a row holds 4 dwords of the activations, so one 16-byte load per lane per chunk gives
-// the whole row the chunk's 64 dwords.  The x registers come straight from vector loads (no VALU
-// write precedes the DPP read, so no extra wait states are needed).
-template <int N>
-MOE_INLINE float dot2_bcast(float acc, uint32_t w, uint32_t x) {
-  asm("v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-      : "+v"(acc)
-      : "v"(x), "v"(w), "i"(N));
-  return acc;
+// The 16 products of one 32-column word for one token, with the activations broadcast across
+// each 16-lane row by DPP row_newbcast: every lane of a row holds 4 dwords of the chunk's
+// activations (one 16-byte load per lane), so dword 4g + c of word JW sits in component c of
+// lane 4 JW + g.  a[g] += dot(w[4g + c], x.c broadcast from lane 4 JW + g).
+//
+// Two hazards the compiler cannot see inside the asm are covered here:
+//   * a DPP instruction must come at least two wait states after any VALU write of a VGPR it
+//     reads (its accumulator included): the block opens with s_nop 1;
+//   * the result of a DOT instruction may be read by another instruction only three wait
+//     states later (the same DOT opcode may take it back as its accumulator at once): the
+//     block closes with s_nop 2, and the four accumulators rotate so that each is written by
+//     a product and read again by the same opcode four instructions later.
+template <int JW>
+MOE_INLINE void dot16_bcast(float (&a)[4], const uint32_t (&w)[16], const u32x4& x) {
+  asm("s_nop 1\n\t"
+      "v_dot2c_f32_f16_dpp %0, %4, %8 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %1, %4, %12 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %2, %4, %16 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %3, %4, %20 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %0, %5, %9 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %1, %5, %13 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %2, %5, %17 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %3, %5, %21 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %0, %6, %10 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %1, %6, %14 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %2, %6, %18 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %3, %6, %22 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %0, %7, %11 row_newbcast:%24 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %1, %7, %15 row_newbcast:%25 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %2, %7, %19 row_newbcast:%26 row_mask:0xf bank_mask:0xf\n\t"
+      "v_dot2c_f32_f16_dpp %3, %7, %23 row_newbcast:%27 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 2"
+      : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+      : "v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w),
+        "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]),
+        "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]),
+        "i"(4 * JW), "i"(4 * JW + 1), "i"(4 * JW + 2), "i"(4 * JW + 3));
 }
 
 // Reduce the four wavefronts' partial sums (fixed order: wave 0 + 1 + 2 + 3) and apply the
@@ -332,10 +357,11 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
         if (t < ng) {
           if (it.shared) {
             const float s = A.shared_scale ? cview<float>(A.shared_scale)[g0 + t] : 1.0f;
-            A.part_shared[static_cast<size_t>(g0 + t) * A.H + it.r0 + lane] = s * h;
+            A.part_shared[(static_cast<size_t>(it.seg) * A.T + g0 + t) * A.H + it.r0 + lane] = s * h;
           } else {
             const int p = uniform(cview<int32_t>(A.pairs)[it.src_base + g0 + t]);
-            A.part[static_cast<size_t>(p) * A.H + it.r0 + lane] = cview<float>(A.gates)[p] * h;
+            A.part[(static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H + it.r0 + lane] =
+                cview<float>(A.gates)[p] * h;
           }
         }
       } else {
@@ -366,20 +392,33 @@ MOE_INLINE bool decode_item(const KArgs& A, int i, int sh_tiles, int tiles, Item
     it.n = A.T;
     it.src_base = 0;
     it.shared = false;
+    it.seg = 0;
+    it.c0 = 0;
+    it.nc = b.cols / kColChunk;
   } else {
-    if (i < sh_tiles) {
+    // segments exist for down items only (the SiLU epilogue of gate_up needs whole rows)
+    const int ssh = MODE == kDown ? A.segs_shared : 1;
+    const int srt = MODE == kDown ? A.segs : 1;
+    int nseg;
+    if (i < sh_tiles * ssh) {
       b = A.shared[MODE];
       it.shared = true;
-      it.r0 = i * kTileRows;
+      it.r0 = (i / ssh) * kTileRows;
+      it.seg = i - (i / ssh) * ssh;
+      nseg = ssh;
       it.n = A.T;
       it.src_base = 0;
       inter = A.I_shared;
     } else {
-      const int a = (i - sh_tiles) / tiles, tile = (i - sh_tiles) - a * tiles;
+      const int r = i - sh_tiles * ssh;
+      const int per = tiles * srt;
+      const int a = r / per, rem = r - a * per, tile = rem / srt;
       it.expert = uniform(cview<int32_t>(A.active)[a]);
       b = A.table[it.expert * 2 + MODE];
       it.shared = false;
       it.r0 = tile * kTileRows;
+      it.seg = rem - tile * srt;
+      nseg = srt;
       it.src_base = uniform(cview<int32_t>(A.offsets)[it.expert]);
       it.n = uniform(cview<int32_t>(A.offsets)[it.expert + 1]) - it.src_base;
       inter = A.I;
@@ -387,6 +426,9 @@ MOE_INLINE bool decode_item(const KArgs& A, int i, int sh_tiles, int tiles, Item
     const int want_rows = MODE == kGateUp ? 2 * inter : A.H;
     const int want_cols = MODE == kGateUp ? A.H : inter;
     if (!block_ok(b, want_rows, want_cols)) return false;
+    const int nc4 = want_cols / kColChunk;
+    it.c0 = uniform(it.seg * nc4 / nseg);
+    it.nc = uniform((it.seg + 1) * nc4 / nseg) - it.c0;
   }
   it.row_hi = MODE == kGateUp ? inter + it.r0 : it.r0 + 32;
   it.planes = b.planes;
@@ -494,8 +536,8 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
   const int nc4 = C / kColChunk;
   S.pbase = gview<u32x4>(it.planes) + static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
   S.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
-  S.cb = uniform((nc4 * wave) / kWavesPerTile);
-  S.ce = uniform((nc4 * (wave + 1)) / kWavesPerTile);
+  S.cb = uniform(it.c0 + (it.nc * wave) / kWavesPerTile);
+  S.ce = uniform(it.c0 + (it.nc * (wave + 1)) / kWavesPerTile);
   const int n = lane < 16 ? lane : lane - 48;
   const bool real = (lane < 16 || lane >= 48) && n < ng;
   const uint16_t* base;
@@ -541,32 +583,41 @@ MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, i
     }
     const int col = lane & 31;
     const int half = col >> 4, tok = col & 15;
+    const bool live = tok < ng && (MODE != kGateUp || half == 0);
+    // this lane's output row base and scale, computed once (rows r0 + 32*half + m follow)
+    uint16_t* act_dst = nullptr;
+    float* out_dst = nullptr;
+    float scale = 1.0f;
+    if (live) {
+      if constexpr (MODE == kGateUp) {
+        act_dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + tok) * A.I_shared + it.r0
+                            : A.act + static_cast<size_t>(it.src_base + g0 + tok) * A.I + it.r0;
+      } else if constexpr (MODE == kDown) {
+        if (it.shared) {
+          if (A.shared_scale) scale = A.shared_scale[g0 + tok];
+          out_dst = A.part_shared + (static_cast<size_t>(it.seg) * A.T + g0 + tok) * A.H;
+        } else {
+          const int p = A.pairs[it.src_base + g0 + tok];
+          scale = A.gates[p];
+          out_dst = A.part + (static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H;
+        }
+        out_dst += it.r0 + 32 * half;
+      } else {
+        out_dst = A.y_plain + static_cast<size_t>(g0 + tok) * it.rows + it.r0 + 32 * half;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       const float v = acc[i];
       if constexpr (MODE == kGateUp) {
         const float up = __shfl_down(v, 16, 64);  // same m, row 32 + m, held 16 lanes up
-        if (half == 0 && tok < ng) {
+        if (live) {
           const float a = v / (1.0f + expf(-v)) * up;  // SiLU(gate) * up
-          const int Iw = it.shared ? A.I_shared : A.I;
-          uint16_t* dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + tok) * Iw
-                                    : A.act + static_cast<size_t>(it.src_base + g0 + tok) * Iw;
-          dst[it.r0 + m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
-        }
-      } else if constexpr (MODE == kDown) {
-        if (tok < ng) {
-          const int r = it.r0 + 32 * half + m;
-          if (it.shared) {
-            const float s = A.shared_scale ? A.shared_scale[g0 + tok] : 1.0f;
-            A.part_shared[static_cast<size_t>(g0 + tok) * A.H + r] = s * v;
-          } else {
-            const int p = A.pairs[it.src_base + g0 + tok];
-            A.part[static_cast<size_t>(p) * A.H + r] = A.gates[p] * v;
-          }
+          act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
         }
       } else {
-        if (tok < ng) A.y_plain[static_cast<size_t>(g0 + tok) * it.rows + it.r0 + 32 * half + m] = v;
+        if (live) out_dst[m] = scale * v;
       }
     }
   }
@@ -629,8 +680,8 @@ MOE_INLINE void make_geo(const KArgs& A, const Item& it, Geo& G) {
   const int nc4 = C / kColChunk;
   G.pbase = gview<u32x4>(it.planes) + static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
   G.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
-  G.cb = uniform((nc4 * wave) / kWavesPerTile);
-  G.n = uniform((nc4 * (wave + 1)) / kWavesPerTile) - G.cb;
+  G.cb = uniform(it.c0 + (it.nc * wave) / kWavesPerTile);
+  G.n = uniform(it.c0 + (it.nc * (wave + 1)) / kWavesPerTile) - G.cb;
   G.ng = it.n;
 #pragma unroll
   for (int t = 0; t < kMaxTokGroup; ++t) {
@@ -685,35 +736,16 @@ MOE_INLINE void pick_refill(const Geo& cur, const Geo& nxt, bool cont, int v, in
 
 // Products of one 32-column word for the ng (<= 4) tokens of the ring slot.
 template <int Q, int JW>
-MOE_INLINE void ring_word(const Ring<Q>& R, int s, int ng, uint32_t lane4, float (&acc)[kMaxTokGroup]) {
+MOE_INLINE void ring_word(const Ring<Q>& R, int s, int ng, uint32_t lane4,
+                          float (&acc)[kMaxTokGroup][4]) {
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = word_of(R.buf[s][p], JW);
   uint32_t wv[16];
   decode_word<Q>(w, lane4, wv);
 #pragma unroll
-  for (int t = 0; t < kMaxTokGroup; ++t) {
-    if (t < ng) {
-      const u32x4& xv = R.xbuf[s][t];
-      // dword d of word JW is dword 16*JW + d of the chunk: lane 4*JW + d/4, component d%4
-      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[0], xv.x);
-      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[1], xv.y);
-      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[2], xv.z);
-      acc[t] = dot2_bcast<4 * JW + 0>(acc[t], wv[3], xv.w);
-      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[4], xv.x);
-      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[5], xv.y);
-      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[6], xv.z);
-      acc[t] = dot2_bcast<4 * JW + 1>(acc[t], wv[7], xv.w);
-      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[8], xv.x);
-      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[9], xv.y);
-      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[10], xv.z);
-      acc[t] = dot2_bcast<4 * JW + 2>(acc[t], wv[11], xv.w);
-      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[12], xv.x);
-      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[13], xv.y);
-      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[14], xv.z);
-      acc[t] = dot2_bcast<4 * JW + 3>(acc[t], wv[15], xv.w);
-    }
-  }
+  for (int t = 0; t < kMaxTokGroup; ++t)
+    if (t < ng) dot16_bcast<JW>(acc[t], wv, R.xbuf[s][t]);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -760,7 +792,7 @@ MOE_INLINE void valu_stream(const KArgs& A, int& i, Item& it, int total, int sh_
     write_table<Q>(L, lane, wave);
     __syncthreads();
     if (cont) prefetch_lut_q<Q>(next, lane, wave, L);
-    float acc[kMaxTokGroup] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[kMaxTokGroup][4] = {};
     // the wavefront walks its chunks padded to a multiple of D, so the next item's chunk k
     // always lands in slot k % D
     const int m = (cur.n + D - 1) / D * D;
@@ -780,7 +812,10 @@ MOE_INLINE void valu_stream(const KArgs& A, int& i, Item& it, int total, int sh_
         R.issue(s, g, k);
       }
     }
-    reduce_and_store<MODE, kMaxTokGroup>(A, it, 0, it.n, acc);
+    float tot[kMaxTokGroup];
+#pragma unroll
+    for (int t = 0; t < kMaxTokGroup; ++t) tot[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
+    reduce_and_store<MODE, kMaxTokGroup>(A, it, 0, it.n, tot);
     i = j;
     it = next;
     if (!cont) return;
@@ -800,7 +835,9 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
     tiles = (MODE == kGateUp ? A.I : A.H) / kTileRows;
     n_routed = uniform(cview<int32_t>(A.n_active)[0]);
   }
-  const int total = sh_tiles + n_routed * tiles;
+  const int ssh = MODE == kDown ? A.segs_shared : 1;
+  const int srt = MODE == kDown ? A.segs : 1;
+  const int total = sh_tiles * ssh + n_routed * tiles * srt;
   Item it;
   int i = next_item<MODE>(A, static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x), total,
                           sh_tiles, tiles, it);

@@ -6,8 +6,8 @@ namespace moeapq {
 namespace apq {
 int launch_gate_up(const KArgs& k, int max_items, hipStream_t stream);
 int launch_down(const KArgs& k, int max_items, hipStream_t stream);
-int launch_combine(const float* part, const float* part_shared, int T, int H, int k, uint16_t* y,
-                   hipStream_t stream);
+int launch_combine(const float* part, const float* part_shared, int T, int H, int k, int segs,
+                   int segs_shared, uint16_t* y, hipStream_t stream);
 int launch_plain(const KArgs& k, int max_items, hipStream_t stream);
 int launch_decode(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
 }  // namespace apq
@@ -28,9 +28,12 @@ int launch_apq_ffn(const FfnArgs& a, hipStream_t stream) {
   const int sh = a.shared ? 1 : 0;
   const int gu_items = sh * (a.I_shared / kGateUpTileRows) + a.E * (a.I / kGateUpTileRows);
   if (int rc = apq::launch_gate_up(k, gu_items, stream)) return rc;
-  const int dn_items = (sh + a.E) * (a.H / kRowPanel);
+  k.segs = a.ws.segs;
+  k.segs_shared = sh ? a.ws.segs_shared : 1;
+  const int dn_items = (sh * k.segs_shared + a.E * k.segs) * (a.H / kRowPanel);
   if (int rc = apq::launch_down(k, dn_items, stream)) return rc;
-  return apq::launch_combine(a.ws.part, sh ? a.ws.part_shared : nullptr, a.T, a.H, a.k, a.y, stream);
+  return apq::launch_combine(a.ws.part, sh ? a.ws.part_shared : nullptr, a.T, a.H, a.k, k.segs,
+                             k.segs_shared, a.y, stream);
 }
 
 int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y,
@@ -40,6 +43,7 @@ int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y
   k.T = T;
   k.x = x;
   k.y_plain = y;
+  k.segs = k.segs_shared = 1;
   k.dense_threshold = dense_threshold > 0 ? dense_threshold : kDefaultDenseThreshold;
   return apq::launch_plain(k, blk.rows / kRowPanel, stream);
 }

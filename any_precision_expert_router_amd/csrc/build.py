@@ -73,6 +73,9 @@ def _check_isa(tmp: str) -> None:
         total += n
         if problems:
             raise RuntimeError(f"DPP hazards in {os.path.basename(path)}:\n" + "\n".join(problems[:20]))
+        spills = isa_check.scratch_users(path)
+        if spills:
+            raise RuntimeError(f"register spills (scratch memory) in {os.path.basename(path)}: {spills}")
     if total == 0:
         raise RuntimeError("no DPP instructions found in the device assembly: ISA check did not run")
 

@@ -46,11 +46,24 @@ struct Workspace {
   int32_t* n_active;     // [1]
   uint16_t* act;         // fp16 [T*k][I]    SiLU-gated activations, sorted-pair order
   uint16_t* act_shared;  // fp16 [T][I_shared]
-  float* part;           // fp32 [T*k][H]    gate-scaled expert outputs, pair order
-  float* part_shared;    // fp32 [T][H]      scaled shared-expert outputs
+  float* part;           // fp32 [segs][T*k][H]  gate-scaled expert outputs, pair order
+  float* part_shared;    // fp32 [segs_sh][T][H] scaled shared-expert outputs
+  int segs, segs_shared; // down column segments (down_segments)
   size_t bytes;          // total bytes the layout needs
 };
 Workspace carve_workspace(void* base, int T, int E, int H, int I, int k, int I_shared);
+
+// Column segments of a down row tile.  In decode-size batches a long down row (e.g. the shared
+// expert's 5632 columns) is split so that no work item carries much more than kSegChunks
+// 128-column chunks; each segment writes its own fp32 partial sums, which the combine adds in a
+// fixed order.  Batches with many pairs already have enough items and keep whole rows.
+constexpr int kSegChunks = 16;
+constexpr int kSegMaxPairs = 512;
+inline int down_segments(int cols, int pairs) {
+  const int nc4 = cols / kColChunk;
+  if (pairs > kSegMaxPairs || nc4 <= kSegChunks + kSegChunks / 2) return 1;
+  return (nc4 + kSegChunks - 1) / kSegChunks;
+}
 
 // ---- launchers (return MOE_OK or an error code with the message set) -------------------------
 int launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* gates,

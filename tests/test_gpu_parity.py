@@ -140,10 +140,12 @@ def test_decode_indices_bit_exact(q):
 @pytest.mark.parametrize("dense", [0, 1], ids=["auto", "mfma"])
 @pytest.mark.parametrize("q", range(1, 9))
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 16, 17, 40])
-def test_gemv_matches_oracle(q, T, dense):
-    """Both product paths (packed-dot VALU below the dense threshold, MFMA at or above it)."""
-    say(f"gemv q={q} T={T} dense={dense}")
-    R, C = 128, 640
+@pytest.mark.parametrize("C", [640, 2176])
+def test_gemv_matches_oracle(q, T, dense, C):
+    """Both product paths (packed-dot VALU below the dense threshold, MFMA at or above it).
+    C = 2176 gives every wavefront 4 or 5 chunks, more than the deepest chunk ring holds."""
+    say(f"gemv q={q} T={T} dense={dense} C={C}")
+    R = 128
     r = np.random.default_rng(q * 100 + T)
     idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
     lut = (np.sort(r.standard_normal((R, 1 << q)), axis=1) * 0.02).astype(np.float16)
@@ -157,13 +159,18 @@ def test_gemv_matches_oracle(q, T, dense):
 
 @pytest.mark.parametrize("dense", [1000, 1], ids=["valu", "mfma"])
 @pytest.mark.parametrize("q", range(1, 9))
-def test_gemv_one_hot_probe_is_exact_lut_read(q, dense):
-    """x = e_c gives y_r = LUT_r[idx_q(r, c)] exactly: pins the decode through the GEMV."""
-    R, C = 64, 256
+@pytest.mark.parametrize("C", [256, 2048])
+def test_gemv_one_hot_probe_is_exact_lut_read(q, dense, C):
+    """x = e_c gives y_r = LUT_r[idx_q(r, c)] exactly: pins the decode through the GEMV.
+    At C = 2048 every wavefront walks 4 chunks; every column of its last chunk is probed."""
+    R = 64
     r = np.random.default_rng(50 + q)
     idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
     lut = r.standard_normal((R, 1 << q)).astype(np.float16)
-    cols = [0, 1, 31, 32, 77, 128, 200, 255]
+    if C == 256:
+        cols = [0, 1, 31, 32, 77, 128, 200, 255]
+    else:
+        cols = list(range(384, 512)) + list(range(1920, 2048)) + [0, 1, 700, 1100]
     x = np.zeros((len(cols), C), dtype=np.float16)
     for t, c in enumerate(cols):
         x[t, c] = 1.0
@@ -225,6 +232,17 @@ def test_layer_with_shared_expert_and_scale(threshold):
     shape = wl.TINY.replace(H=256, E=8, I=256, k=2, T=19, I_shared=512, q_shared=8, name="shared")
     r = np.random.default_rng(3)
     _check_layer(shape, shared_scale=r.uniform(-1, 2, size=shape.T), threshold=threshold)
+
+
+@pytest.mark.parametrize("threshold", [0, 1, 1000], ids=["auto", "all-mfma", "valu-max"])
+def test_layer_long_down_rows_split_into_segments(threshold):
+    """Down rows long enough to be cut into column segments (routed: 26 chunks of 128 columns ->
+    2 segments of 13; shared: 41 chunks -> 3 segments of 13/14/14, every wavefront share ragged),
+    each with its own partial sums, summed by the combine."""
+    shape = wl.TINY.replace(H=128, E=6, I=26 * 128, k=2, T=7, I_shared=41 * 128, q_shared=8,
+                            name="segmented down rows")
+    q = np.array([[3 + (e + m) % 6 for m in range(2)] for e in range(shape.E)], dtype=np.uint8)
+    _check_layer(shape, q_override=q, threshold=threshold)
 
 
 def test_layer_k1_and_k_equals_E():
