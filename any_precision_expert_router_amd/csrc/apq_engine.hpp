@@ -48,14 +48,34 @@ MOE_INLINE const AS_CONST T* cview(const void* p) { return (const AS_CONST T*)p;
 
 constexpr int kThreads = 64 * kWavesPerTile;
 constexpr int kMaxTokGroup = 4;                  // tokens sharing one VALU pass over the weights
-constexpr int kTblWords = 256 * 64;              // [256 entries][64 lanes] uint32
 constexpr int kDenseGroup = 16;                  // tokens per MFMA pass (32x32 tile: 2 row halves x 16)
-constexpr int kRedWords = (kWavesPerTile - 1) * 16 * 64;  // 16 floats per lane per wavefront
-constexpr int kLdsWords = kTblWords + kRedWords;
 
-// The only LDS object of the tile kernels, so the table starts at LDS address 0 and a table
-// address is exactly entry*256 + lane*4.
-static __shared__ uint32_t g_lds[kLdsWords];
+// LDS map of a tile workgroup (bytes):
+//   [0, 64K)        lookup tables, 4-byte slots [entry][64 lanes] unless noted.  Streaming (VALU)
+//                   tiles: the pair table (q <= 4, entries a << 4 | b) or the single table
+//                   (q >= 5).  Dense (MFMA) tiles keep their table below 32K: the pair table for
+//                   q <= 3, the single table for q = 4..7, the single table with 2-byte slots
+//                   for q = 8.
+//   [32K, 64K)      dense tiles only: each wavefront's 8K ring of two staged activation chunks,
+//                   [slot][16 column pieces][16 tokens][16 bytes] fp16, filled by buffer loads
+//                   straight to LDS; after the tile's columns it holds that wavefront's partial
+//                   sums for the cross-wavefront reduction.
+//   [64K, 67K)      streaming tiles: cross-wavefront reduction (4 floats per lane, waves 1-3).
+//   [67K, 67K+16)   the work queue's next item index.
+constexpr uint32_t kTblBytes = 65536;
+constexpr uint32_t kXRingBase = 32768;
+constexpr uint32_t kXSlotBytes = kDenseGroup * kColChunk * 2;   // 4 KiB
+constexpr uint32_t kXWaveBytes = 2 * kXSlotBytes;
+constexpr uint32_t kRedBase = kTblBytes;
+constexpr uint32_t kRedBytes = (kWavesPerTile - 1) * kMaxTokGroup * 64 * 4;
+constexpr uint32_t kQueueBase = kRedBase + kRedBytes;   // the next item index, published by thread 0
+constexpr uint32_t kLdsBytes = kQueueBase + 16;
+static_assert(kXRingBase + kWavesPerTile * kXWaveBytes <= kTblBytes, "activation ring overlaps");
+static_assert(32 * 64 * 4 <= kXWaveBytes, "dense partial sums do not fit a ring");
+
+// The only LDS object of the tile kernels, so it starts at LDS address 0: a table address is
+// exactly entry*256 + lane*4 and an LDS byte offset is an LDS address.
+static __shared__ uint32_t g_lds[kLdsBytes / 4];
 
 enum Mode : int { kGateUp = 0, kDown = 1, kPlain = 2 };
 
@@ -127,6 +147,9 @@ struct Item {
   int expert;    // routed expert id, -1 for the shared expert / plain block
   int c0, nc;    // the item's column chunks [c0, c0 + nc) (a segment of a long down row)
   int seg;       // segment index (selects the partial-sum buffer of a down item)
+  int tok[kRecTok];     // activation rows of the first tokens (gate_up)
+  int pair[kRecTok];    // their pair ids (down partial-sum rows)
+  float gate[kRecTok];  // their gate weights (down)
   bool shared;
 };
 
@@ -150,45 +173,56 @@ struct KArgs {
   int32_t* err;
   int dense_threshold;          // tiles with at least this many tokens take the MFMA path
   int segs, segs_shared;        // column segments per down row tile (routed, shared expert)
+  const ExpertRecord* recs;     // [1 + E]: shared expert, then the active routed experts
+  uint32_t* counter;            // work counter of this launch (null: static round-robin)
 };
+
+// Work queue of a workgroup.  Its first two items are blockIdx.x and blockIdx.x + gridDim.x;
+// the later ones come from its sub-queue's counter, requested by thread 0 one item ahead and published to the workgroup through LDS at the current item's
+// reduction barrier, so the atomic's latency hides behind a whole item.  Without a counter the
+// queue is static round-robin.
+struct Queue {
+  int nxt;            // the item after the current one (uniform)
+  int sub, nsub;      // this workgroup's sub-queue and the number of sub-queues
+  uint32_t pending;   // thread 0: counter value fetched for the item after nxt
+};
+
+// The dynamic items (from 2 * gridDim.x on) are dealt to min(kQueues, gridDim.x) interleaved
+// sub-queues, each with its own counter, so that no single address takes every fetch.
+MOE_INLINE void queue_init(Queue& Qu) {
+  Qu.nxt = static_cast<int>(blockIdx.x + gridDim.x);
+  Qu.nsub = min(kQueues, static_cast<int>(gridDim.x));
+  Qu.sub = static_cast<int>(blockIdx.x) % Qu.nsub;
+  Qu.pending = 0;
+}
+MOE_INLINE void queue_request(const KArgs& A, Queue& Qu) {
+  if (A.counter && threadIdx.x == 0) Qu.pending = atomicAdd(A.counter + Qu.sub * kCounterStride, 1u);
+}
+// Before the barrier: thread 0 publishes the item after nxt.
+MOE_INLINE void queue_publish(const KArgs& A, const Queue& Qu) {
+  if (threadIdx.x == 0) {
+    const int after = A.counter ? 2 * static_cast<int>(gridDim.x) + Qu.sub + Qu.nsub * static_cast<int>(Qu.pending)
+                                : Qu.nxt + static_cast<int>(gridDim.x);
+    *reinterpret_cast<volatile int*>(reinterpret_cast<char*>(g_lds) + kQueueBase) = after;
+  }
+}
+// After the barrier: every thread reads it, the queue moves one item on and requests the next.
+// Returns the item that becomes current.
+MOE_INLINE int queue_advance(const KArgs& A, Queue& Qu) {
+  const int after = uniform(*reinterpret_cast<volatile int*>(reinterpret_cast<char*>(g_lds) + kQueueBase));
+  const int cur = Qu.nxt;
+  Qu.nxt = after;
+  queue_request(A, Qu);
+  return cur;
+}
 
 MOE_INLINE int lane_row(const Item& it, int lane) {
   return lane < 32 ? it.r0 + lane : it.row_hi + (lane - 32);
 }
 
-// Each thread prefetches LUT bytes of its lane's row into registers:
-//   q <= 4: the whole row (2^q fp16, at most 32 bytes), every wavefront (they build different
-//           first indices of the pair table);
+// Each thread prefetches LUT bytes of its lane's row into registers (only those it needs):
+//   q <= 4: the whole row (2^q fp16, at most 32 bytes), every wavefront;
 //   q >= 5: quarter `wave` of the row (2^(q-2) fp16, at most 128 bytes).
-MOE_INLINE void prefetch_lut(const Item& it, int lane, int wave, u32x4 (&L)[kLutRegs]) {
-  const char* row = reinterpret_cast<const char*>(it.lut) +
-                    static_cast<size_t>(lane_row(it, lane)) * (2u << it.q);
-  const AS_GLOBAL char* g = gview<char>(row);
-  switch (it.q) {
-    case 1: L[0].x = *reinterpret_cast<const AS_GLOBAL uint32_t*>(g); break;
-    case 2: {
-      const uint64_t v = *reinterpret_cast<const AS_GLOBAL uint64_t*>(g);
-      L[0].x = static_cast<uint32_t>(v);
-      L[0].y = static_cast<uint32_t>(v >> 32);
-      break;
-    }
-    case 3: L[0] = *reinterpret_cast<const AS_GLOBAL u32x4*>(g); break;
-    case 4:
-      L[0] = reinterpret_cast<const AS_GLOBAL u32x4*>(g)[0];
-      L[1] = reinterpret_cast<const AS_GLOBAL u32x4*>(g)[1];
-      break;
-    default: {
-      const int n4 = 1 << (it.q - 5);  // 1, 2, 4, 8 registers
-      const AS_GLOBAL u32x4* s = reinterpret_cast<const AS_GLOBAL u32x4*>(g) + wave * n4;
-#pragma unroll
-      for (int r = 0; r < kLutRegs; ++r)
-        if (r < n4) L[r] = s[r];
-      break;
-    }
-  }
-}
-
-// The same, for an item whose width is known at compile time (only the registers it needs).
 template <int Q>
 MOE_INLINE void prefetch_lut_q(const Item& it, int lane, int wave, u32x4 (&L)[kLutRegs]) {
   const AS_GLOBAL char* g = gview<char>(reinterpret_cast<const char*>(it.lut) +
@@ -326,14 +360,16 @@ MOE_INLINE void dot16_bcast(float (&a)[4], const uint32_t (&w)[16], const u32x4&
 // Reduce the four wavefronts' partial sums (fixed order: wave 0 + 1 + 2 + 3) and apply the
 // epilogue of the mode for the ng real tokens of the group starting at g0.
 template <int MODE, int NT>
-MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, float (&acc)[NT]) {
+MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, float (&acc)[NT],
+                                 const Queue& Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  float* red = reinterpret_cast<float*>(g_lds + kTblWords);
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(g_lds) + kRedBase);
   if (wave > 0) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[((wave - 1) * kMaxTokGroup + t) * 64 + lane] = acc[t];
   }
+  queue_publish(A, Qu);
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
@@ -359,9 +395,9 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
             const float s = A.shared_scale ? cview<float>(A.shared_scale)[g0 + t] : 1.0f;
             A.part_shared[(static_cast<size_t>(it.seg) * A.T + g0 + t) * A.H + it.r0 + lane] = s * h;
           } else {
-            const int p = uniform(cview<int32_t>(A.pairs)[it.src_base + g0 + t]);
-            A.part[(static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H + it.r0 + lane] =
-                cview<float>(A.gates)[p] * h;
+            // the streaming path holds at most kRecTok tokens, all described by the record
+            const int p = it.pair[t];
+            A.part[(static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H + it.r0 + lane] = it.gate[t] * h;
           }
         }
       } else {
@@ -372,22 +408,16 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
   __syncthreads();
 }
 
-MOE_INLINE bool block_ok(const moe_apq_block& b, int rows, int cols) {
-  const uintptr_t align = reinterpret_cast<uintptr_t>(b.planes) | reinterpret_cast<uintptr_t>(b.lut);
-  return b.planes != nullptr && b.lut != nullptr && (align & 15) == 0 && b.rows == rows &&
-         b.cols == cols && b.q >= 1 && b.q <= 8 && b.state == MOE_PAGE_GPU;
-}
-
 // Item i of the launch's list: shared-expert tiles first (they carry every token), then the
-// routed experts' tiles.  Returns false (and records the block) if its descriptor is invalid.
+// routed experts' tiles, each described by its expert record.  Returns false if the record says
+// a page-table descriptor is invalid.
 template <int MODE>
 MOE_INLINE bool decode_item(const KArgs& A, int i, int sh_tiles, int tiles, Item& it) {
   constexpr int kTileRows = MODE == kGateUp ? kGateUpTileRows : kRowPanel;
-  moe_apq_block b;
   int inter = 0;
   it.expert = -1;
   if constexpr (MODE == kPlain) {
-    b = A.plain;
+    const moe_apq_block& b = A.plain;
     it.r0 = i * kRowPanel;
     it.n = A.T;
     it.src_base = 0;
@@ -395,138 +425,263 @@ MOE_INLINE bool decode_item(const KArgs& A, int i, int sh_tiles, int tiles, Item
     it.seg = 0;
     it.c0 = 0;
     it.nc = b.cols / kColChunk;
+    it.planes = b.planes;
+    it.lut = b.lut;
+    it.rows = b.rows;
+    it.cols = b.cols;
+    it.q = b.q;
+#pragma unroll
+    for (int t = 0; t < kRecTok; ++t) {
+      it.tok[t] = t;
+      it.pair[t] = t;
+      it.gate[t] = 1.0f;
+    }
   } else {
     // segments exist for down items only (the SiLU epilogue of gate_up needs whole rows)
     const int ssh = MODE == kDown ? A.segs_shared : 1;
     const int srt = MODE == kDown ? A.segs : 1;
-    int nseg;
+    int nseg, slot;
     if (i < sh_tiles * ssh) {
-      b = A.shared[MODE];
+      slot = 0;
       it.shared = true;
       it.r0 = (i / ssh) * kTileRows;
       it.seg = i - (i / ssh) * ssh;
       nseg = ssh;
-      it.n = A.T;
-      it.src_base = 0;
       inter = A.I_shared;
     } else {
       const int r = i - sh_tiles * ssh;
       const int per = tiles * srt;
       const int a = r / per, rem = r - a * per, tile = rem / srt;
-      it.expert = uniform(cview<int32_t>(A.active)[a]);
-      b = A.table[it.expert * 2 + MODE];
+      slot = 1 + a;
       it.shared = false;
       it.r0 = tile * kTileRows;
       it.seg = rem - tile * srt;
       nseg = srt;
-      it.src_base = uniform(cview<int32_t>(A.offsets)[it.expert]);
-      it.n = uniform(cview<int32_t>(A.offsets)[it.expert + 1]) - it.src_base;
       inter = A.I;
     }
-    const int want_rows = MODE == kGateUp ? 2 * inter : A.H;
-    const int want_cols = MODE == kGateUp ? A.H : inter;
-    if (!block_ok(b, want_rows, want_cols)) return false;
-    const int nc4 = want_cols / kColChunk;
+    const AS_CONST ExpertRecord& rec = cview<ExpertRecord>(A.recs)[slot];
+    it.planes = rec.planes[MODE];
+    it.lut = rec.lut[MODE];
+    it.q = rec.q[MODE];
+    it.expert = rec.expert;
+    it.src_base = rec.src_base;
+    it.n = rec.n;
+#pragma unroll
+    for (int t = 0; t < kRecTok; ++t) {
+      it.tok[t] = rec.tok[t];
+      it.pair[t] = rec.pair[t];
+      it.gate[t] = rec.gate[t];
+    }
+    it.rows = MODE == kGateUp ? 2 * inter : A.H;
+    it.cols = MODE == kGateUp ? A.H : inter;
+    if (!rec.ok) return false;
+    const int nc4 = it.cols / kColChunk;
     it.c0 = uniform(it.seg * nc4 / nseg);
     it.nc = uniform((it.seg + 1) * nc4 / nseg) - it.c0;
   }
   it.row_hi = MODE == kGateUp ? inter + it.r0 : it.r0 + 32;
-  it.planes = b.planes;
-  it.lut = b.lut;
-  it.rows = b.rows;
-  it.cols = b.cols;
-  it.q = b.q;
   return true;
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense tiles (many tokens on one block: the shared expert, hot experts): matrix-core path.
+// Dense tiles (many tokens on one block: the shared expert, hot experts, prefill): matrix cores.
 //
-// The weights are decoded exactly as above (one row per lane, 64 rows); the products go to
-// v_mfma_f32_32x32x16_f16.  Its A operand is a lane's 8 decoded weights of one 8-column octet,
-// so lanes 0-31 feed rows 0-31 as k 0-7 and lanes 32-63 feed rows 32-63 as k 8-15.  The B
-// operand separates the two row halves in the N dimension: column n < 16 carries token n on
-// k 0-7 (zero on k 8-15), column 16 + n carries token n on k 8-15 (zero on k 0-7).  One MFMA
-// per octet thus computes all 64 rows for 16 tokens: D[m][n] = row m . x_n and
-// D[m][16 + n] = row 32 + m . x_n.  B lanes that carry zeros use out-of-range buffer offsets,
-// which read as zero without touching memory.
+// The weights are decoded as in the streaming path, one row per lane, 64 rows.  For a pair of
+// 8-column octets (o, o + 1) a lane holds X = its row's octet o and Y = its row's octet o + 1;
+// one v_permlane32_swap per register turns them into the two A operands of
+// v_mfma_f32_32x32x16_f16: [X of lanes 0-31, Y of lanes 0-31] = rows 0-31 with k 0-7 = octet o
+// and k 8-15 = octet o + 1, and [X of lanes 32-63, Y of lanes 32-63] = rows 32-63 likewise.
+// The B operand is the same for both: lane n < 32 holds token n % 16's octet o, lane 32 + n its
+// octet o + 1 (columns 16-31 repeat tokens 0-15 and are dropped).  Two MFMAs per octet pair
+// therefore compute all 64 rows for 16 tokens with no zero padding.
+//
+// Activations are staged per 128-column chunk into the wavefront's LDS ring by buffer loads
+// that write LDS directly, issued just before the same chunk's plane loads: vector memory
+// completes in order, so one wait covers both.  The ring is piece-major ([piece][token]), so a
+// B operand is one contiguous 1-KiB ds_read_b128 with no bank conflicts.
 // ---------------------------------------------------------------------------------------------
+
+// Table kind of dense tiles: 0 = pair (q <= 3), 1 = single with 4-byte slots (q = 4..7),
+// 2 = single with 2-byte slots (q = 8).
+template <int Q>
+constexpr int dense_table_kind() { return Q <= 3 ? 0 : (Q <= 7 ? 1 : 2); }
+
+// q <= 4 single table: every wavefront holds the whole row; wavefront W writes entries
+// [W VPW, (W+1) VPW).
+template <int Q, int W>
+MOE_INLINE void write_small_single_rows(const u32x4 (&L)[kLutRegs], int lane) {
+  constexpr int NE = 1 << Q;
+  constexpr int VPW = NE >= 4 ? NE / 4 : 1;
+  char* base = reinterpret_cast<char*>(g_lds) + lane * 4;
+  if constexpr (W * VPW < NE) {
+#pragma unroll
+    for (int vi = 0; vi < VPW; ++vi) {
+      const int v = W * VPW + vi;
+      const uint32_t d = lut_dword(L, v);
+      const uint32_t dup = __builtin_amdgcn_perm(d, d, (v & 1) ? 0x03020302u : 0x01000100u);
+      *reinterpret_cast<uint32_t*>(base + (v << 8)) = dup;
+    }
+  }
+}
+
+// Every address is a per-lane base plus a compile-time offset (one ds_write with an immediate).
+template <int Q>
+MOE_INLINE void write_dense_table(const u32x4 (&L)[kLutRegs], int lane, int wave) {
+  constexpr int NE = 1 << Q;
+  if constexpr (dense_table_kind<Q>() == 0) {
+    write_table<Q>(L, lane, wave);
+  } else if constexpr (dense_table_kind<Q>() == 2) {
+    // registers hold this wavefront's quarter: entries [64 wave, 64 wave + 64), at v*128 + lane*2
+    char* base = reinterpret_cast<char*>(g_lds) + lane * 2 + wave * (64 * 128);
+#pragma unroll
+    for (int vi = 0; vi < 64; ++vi) {
+      const uint32_t d = lut_dword(L, vi);
+      *reinterpret_cast<uint16_t*>(base + vi * 128) = static_cast<uint16_t>((vi & 1) ? d >> 16 : d);
+    }
+  } else if constexpr (Q >= 5) {
+    constexpr int VPW = NE / 4;  // registers hold this wavefront's quarter
+    char* base = reinterpret_cast<char*>(g_lds) + lane * 4 + wave * (VPW << 8);
+#pragma unroll
+    for (int vi = 0; vi < VPW; ++vi) {
+      const uint32_t d = lut_dword(L, vi);
+      *reinterpret_cast<uint32_t*>(base + (vi << 8)) =
+          __builtin_amdgcn_perm(d, d, (vi & 1) ? 0x03020302u : 0x01000100u);
+    }
+  } else {
+    switch (wave) {
+      case 0: write_small_single_rows<Q, 0>(L, lane); break;
+      case 1: write_small_single_rows<Q, 1>(L, lane); break;
+      case 2: write_small_single_rows<Q, 2>(L, lane); break;
+      default: write_small_single_rows<Q, 3>(L, lane); break;
+    }
+  }
+}
+
+MOE_INLINE uint32_t lds_u16(uint32_t byte_addr) {
+  return *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(g_lds) + byte_addr);
+}
+
+// One 32-column word through the dense table: dword 4b + j = (column 8b + 2j, column 8b + 2j + 1).
+template <int Q>
+MOE_INLINE void decode_word_dense(const uint32_t (&w)[Q], uint32_t lane4, uint32_t (&wv)[16]) {
+  if constexpr (dense_table_kind<Q>() == 0) {
+    decode_word<Q>(w, lane4, wv);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t we = single_word<Q>(w, j), wo = single_word<Q>(w, j + 4);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if constexpr (dense_table_kind<Q>() == 2) {
+          const uint32_t lo = lds_u16(tbl_addr(we, lane4, b) >> 1);
+          const uint32_t hi = lds_u16(tbl_addr(wo, lane4, b) >> 1);
+          wv[4 * b + j] = lo | (hi << 16);
+        } else {
+          const uint32_t ve = lds_load(tbl_addr(we, lane4, b));
+          const uint32_t vo = lds_load(tbl_addr(wo, lane4, b));
+          wv[4 * b + j] = __builtin_amdgcn_perm(vo, ve, 0x05040100u);  // (even lo, odd hi)
+        }
+      }
+    }
+  }
+}
+
+// 16 bytes per lane from `rsrc` at voff + soff straight into LDS at m0 + 16 * lane.  The
+// compiler does not see this load, so it is counted by hand (dense_wait).  The lgkmcnt wait
+// makes sure the LDS reads of the slot's previous chunk have returned before it is refilled.
+// M0 is set here without the compiler's knowledge; the build checks that no compiler-generated
+// instruction of these kernels reads M0.
+MOE_INLINE void lds_dma16(uint32_t lds_addr, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+
 template <int Q>
 struct DenseStream {
-  static constexpr int D = 2;
-  u32x4 buf[D][Q];       // plane units of a chunk
-  u32x4 xw[2][4];        // B operand of a word (4 octets), double-buffered by word parity
+  static constexpr int D = 2;       // chunks in flight per wavefront
+  static constexpr int kDma = 4;    // LDS loads per staged chunk (4 column pieces x 16 tokens)
+  u32x4 buf[D][Q];                  // plane units of a chunk
   const AS_GLOBAL u32x4* pbase;
   size_t plane_u4;
-  __amdgpu_buffer_rsrc_t xrsrc;
-  uint32_t xoff;         // byte offset of this lane's token row (out of range: zero lane)
   int cb, ce;
+  __amdgpu_buffer_rsrc_t xrsrc;
+  uint32_t rowoff[kDma];            // per lane: DMA i's byte offset (token lane%16, piece 4i + lane/16)
+  uint32_t xring;                   // LDS address of this wavefront's ring
+  uint32_t bx;                      // per lane: B-operand address in slot 0, piece 0
 
-  MOE_INLINE void issue_planes(int slot, int c) {
+  // Loads are issued unconditionally (a chunk past the end re-reads the last one, a cache hit)
+  // so that the number of loads in flight is always the same.
+  MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
+  // Activations of chunk c into slot `slot`, then its planes.
+  MOE_INLINE void issue(int slot, int c) {
+#pragma unroll
+    for (int i = 0; i < kDma; ++i)
+      lds_dma16(xring + slot * kXSlotBytes + i * 1024, rowoff[i], xrsrc, static_cast<uint32_t>(c) * 256u);
 #pragma unroll
     for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u4 + static_cast<size_t>(c) * 64];
   }
-  MOE_INLINE void issue_x(int wslot, int c, int jw) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      xw[wslot][b] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   xrsrc, xoff + static_cast<uint32_t>(c * 256 + jw * 64 + b * 16), 0, 0));
-  }
-  // Loads are issued unconditionally (a chunk past the end re-reads the last one, a cache hit)
-  // so that the number of loads in flight never depends on run-time branches.
-  MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
   MOE_INLINE void prologue() {
 #pragma unroll
-    for (int s = 0; s < D; ++s) issue_planes(s, clamp(cb + s));
-    issue_x(0, clamp(cb), 0);
+    for (int s = 0; s < D; ++s) issue(s, clamp(cb + s));
   }
 };
 
+// The staged activations of the chunk about to be consumed have landed: after them were issued
+// its own planes, the next chunk's activations and the next chunk's planes.
+template <int Q>
+MOE_INLINE void dense_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * Q + DenseStream<Q>::kDma) : "memory");
+}
+
 template <int Q, int JW>
-MOE_INLINE void dense_word(const DenseStream<Q>& S, int s, uint32_t lane4, f32x16& acc) {
+MOE_INLINE void dense_word(const DenseStream<Q>& S, int s, uint32_t lane4, f32x16& lo, f32x16& hi) {
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = word_of(S.buf[s][p], JW);
   uint32_t wv[16];
-  decode_word<Q>(w, lane4, wv);
+  decode_word_dense<Q>(w, lane4, wv);
+  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kXSlotBytes;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const u32x4 a = {wv[4 * b], wv[4 * b + 1], wv[4 * b + 2], wv[4 * b + 3]};  // columns 8b..8b+7
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
-                                                  __builtin_bit_cast(half8_t, S.xw[JW & 1][b]),
-                                                  acc, 0, 0, 0);
+  for (int pr = 0; pr < 2; ++pr) {
+    // octets o = 2 pr and o + 1 of this word: columns 16 pr .. 16 pr + 15
+    uint32_t a1[4], a2[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(wv[8 * pr + r], wv[8 * pr + 4 + r], false, false);
+      a1[r] = sw[0];
+      a2[r] = sw[1];
+    }
+    const u32x4 b = *reinterpret_cast<const u32x4*>(xb + (JW * 4 + 2 * pr) * 256);
+    const u32x4 va1 = {a1[0], a1[1], a1[2], a1[3]}, va2 = {a2[0], a2[1], a2[2], a2[3]};
+    lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va1),
+                                                 __builtin_bit_cast(half8_t, b), lo, 0, 0, 0);
+    hi = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va2),
+                                                 __builtin_bit_cast(half8_t, b), hi, 0, 0, 0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-template <int Q, int JW>
-MOE_INLINE void dense_step(DenseStream<Q>& S, int s, int c, uint32_t lane4, f32x16& acc) {
-  // the next word's B operand is requested before this word is decoded
-  if constexpr (JW < 3) S.issue_x((JW + 1) & 1, c, JW + 1);
-  else S.issue_x(0, S.clamp(c + 1), 0);
-  dense_word<Q, JW>(S, s, lane4, acc);
 }
 
 template <int Q>
-MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& acc) {
+MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& lo, f32x16& hi) {
   constexpr int D = DenseStream<Q>::D;
   for (int c0 = S.cb; c0 < S.ce; c0 += D) {
 #pragma unroll
     for (int s = 0; s < D; ++s) {
       const int c = c0 + s;
       if (c < S.ce) {
-        dense_step<Q, 0>(S, s, c, lane4, acc);
-        dense_step<Q, 1>(S, s, c, lane4, acc);
-        dense_step<Q, 2>(S, s, c, lane4, acc);
-        dense_step<Q, 3>(S, s, c, lane4, acc);
-        S.issue_planes(s, S.clamp(c + D));
+        dense_wait<Q>();
+        dense_word<Q, 0>(S, s, lane4, lo, hi);
+        dense_word<Q, 1>(S, s, lane4, lo, hi);
+        dense_word<Q, 2>(S, s, lane4, lo, hi);
+        dense_word<Q, 3>(S, s, lane4, lo, hi);
+        S.issue(s, S.clamp(c + D));
       }
     }
   }
 }
 
-// B-operand source of the tokens [g0, g0 + ng) for this lane: token n = lane (lanes 0-15) or
-// lane - 48 (lanes 48-63); every other lane reads zeros.
+// Geometry of the tile for this wavefront and the activation rows of tokens [g0, g0 + ng).
 template <int MODE, int Q>
 MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng, DenseStream<Q>& S) {
   const int lane = threadIdx.x & 63;
@@ -538,53 +693,72 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
   S.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
   S.cb = uniform(it.c0 + (it.nc * wave) / kWavesPerTile);
   S.ce = uniform(it.c0 + (it.nc * (wave + 1)) / kWavesPerTile);
-  const int n = lane < 16 ? lane : lane - 48;
-  const bool real = (lane < 16 || lane >= 48) && n < ng;
   const uint16_t* base;
   size_t rows_total;
-  int row_index = 0;
   if constexpr (MODE == kGateUp) {
     base = A.x;
     rows_total = A.T;
-    if (real) row_index = it.shared ? g0 + n : A.pairs[it.src_base + g0 + n] / A.k;
   } else if constexpr (MODE == kDown) {
     base = it.shared ? A.act_shared : A.act;
     rows_total = it.shared ? static_cast<size_t>(A.T) : static_cast<size_t>(A.T) * A.k;
-    if (real) row_index = it.shared ? g0 + n : it.src_base + g0 + n;
   } else {
     base = A.x;
     rows_total = A.T;
-    if (real) row_index = g0 + n;
   }
-  const size_t bytes = rows_total * C * 2;
   S.xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
-                                              static_cast<int>(bytes), 0x00020000);
-  S.xoff = real ? static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) : 0x80000000u;
+                                              static_cast<int>(rows_total * C * 2), 0x00020000);
+  // token lane % 16 (tokens past ng re-read token g0's row; their columns are dropped)
+  const int t = lane & 15;
+  const int tt = g0 + (t < ng ? t : 0);
+  int row_index;
+  if constexpr (MODE == kGateUp) {
+    row_index = it.shared ? tt : A.pairs[it.src_base + tt] / A.k;
+  } else if constexpr (MODE == kDown) {
+    row_index = it.shared ? tt : it.src_base + tt;
+  } else {
+    row_index = tt;
+  }
+  const uint32_t rb = static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) + (lane >> 4) * 16u;
+#pragma unroll
+  for (int i = 0; i < DenseStream<Q>::kDma; ++i) S.rowoff[i] = rb + i * 64u;
+  S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
+  S.bx = S.xring + static_cast<uint32_t>(lane & 15) * 16u + static_cast<uint32_t>(lane >> 5) * 256u;
 }
 
 // D layout of the 32x32 MFMA: lane l, register i holds D[m][l % 32] with
-// m = 8 (i / 4) + 4 (l / 32) + i % 4.  Column n < 16 is token n of rows m (tile rows 0-31);
-// column 16 + n is token n of rows 32 + m.
+// m = 8 (i / 4) + 4 (l / 32) + i % 4; `lo` covers tile rows m, `hi` rows 32 + m.  Columns
+// l % 32 < 16 are token l % 16 (the other 16 repeat them).  The partial sums of wavefronts 1-3
+// go through their own (drained) activation rings.
 template <int MODE>
-MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, f32x16& acc) {
+MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, f32x16& lo,
+                                       f32x16& hi, const Queue* Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  float* red = reinterpret_cast<float*>(g_lds + kTblWords);
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the ring's last (re-read) loads
+  float* ring = reinterpret_cast<float*>(reinterpret_cast<char*>(g_lds) + kXRingBase);
   if (wave > 0) {
+    float* mine = ring + wave * (kXWaveBytes / 4);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[((wave - 1) * 16 + i) * 64 + lane] = acc[i];
+    for (int i = 0; i < 16; ++i) {
+      mine[i * 64 + lane] = lo[i];
+      mine[(16 + i) * 64 + lane] = hi[i];
+    }
   }
+  if (Qu) queue_publish(A, *Qu);
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int w = 1; w < kWavesPerTile; ++w) {
+      const float* other = ring + w * (kXWaveBytes / 4);
 #pragma unroll
-      for (int w = 1; w < kWavesPerTile; ++w) acc[i] += red[((w - 1) * 16 + i) * 64 + lane];
+      for (int i = 0; i < 16; ++i) {
+        lo[i] += other[i * 64 + lane];
+        hi[i] += other[(16 + i) * 64 + lane];
+      }
     }
-    const int col = lane & 31;
-    const int half = col >> 4, tok = col & 15;
-    const bool live = tok < ng && (MODE != kGateUp || half == 0);
-    // this lane's output row base and scale, computed once (rows r0 + 32*half + m follow)
+    const int tok = lane & 15;
+    const bool live = (lane & 16) == 0 && tok < ng;
+    // this lane's output row base and scale, computed once (rows r0 + m and r0 + 32 + m follow)
     uint16_t* act_dst = nullptr;
     float* out_dst = nullptr;
     float scale = 1.0f;
@@ -601,23 +775,25 @@ MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, i
           scale = A.gates[p];
           out_dst = A.part + (static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H;
         }
-        out_dst += it.r0 + 32 * half;
+        out_dst += it.r0;
       } else {
-        out_dst = A.y_plain + static_cast<size_t>(g0 + tok) * it.rows + it.r0 + 32 * half;
+        out_dst = A.y_plain + static_cast<size_t>(g0 + tok) * it.rows + it.r0;
       }
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      const float v = acc[i];
       if constexpr (MODE == kGateUp) {
-        const float up = __shfl_down(v, 16, 64);  // same m, row 32 + m, held 16 lanes up
+        // gate row r0 + m and up row row_hi + m meet in the same lane and register
         if (live) {
-          const float a = v / (1.0f + expf(-v)) * up;  // SiLU(gate) * up
-          act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(a));
+          const float g = lo[i];
+          act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(g / (1.0f + expf(-g)) * hi[i]));
         }
       } else {
-        if (live) out_dst[m] = scale * v;
+        if (live) {
+          out_dst[m] = scale * lo[i];
+          out_dst[32 + m] = scale * hi[i];
+        }
       }
     }
   }
@@ -625,15 +801,15 @@ MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, i
 }
 
 template <int MODE, int Q>
-MOE_INLINE void run_item_dense(const KArgs& A, const Item& it) {
+MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   u32x4 L[kLutRegs];
-  prefetch_lut(it, lane, wave, L);
+  prefetch_lut_q<Q>(it, lane, wave, L);
   DenseStream<Q> S;
   make_dense_stream<MODE, Q>(A, it, 0, min(kDenseGroup, it.n), S);
   S.prologue();
-  write_table<Q>(L, lane, wave);
+  write_dense_table<Q>(L, lane, wave);
   __syncthreads();
   for (int g0 = 0; g0 < it.n; g0 += kDenseGroup) {
     const int ng = min(kDenseGroup, it.n - g0);
@@ -641,17 +817,17 @@ MOE_INLINE void run_item_dense(const KArgs& A, const Item& it) {
       make_dense_stream<MODE, Q>(A, it, g0, ng, S);
       S.prologue();
     }
-    f32x16 acc = {};
-    dense_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, acc);
-    dense_reduce_and_store<MODE>(A, it, g0, ng, acc);
+    f32x16 lo = {}, hi = {};
+    dense_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, lo, hi);
+    dense_reduce_and_store<MODE>(A, it, g0, ng, lo, hi, g0 + kDenseGroup >= it.n ? &Qu : nullptr);
   }
 }
 
 // A tile that does not stream (at least as many tokens as the dense threshold, or more than 4):
 // matrix-core path.
 template <int MODE, int Q>
-MOE_INLINE void run_item(const KArgs& A, const Item& it) {
-  run_item_dense<MODE, Q>(A, it);
+MOE_INLINE void run_item(const KArgs& A, const Item& it, const Queue& Qu) {
+  run_item_dense<MODE, Q>(A, it, Qu);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -688,8 +864,7 @@ MOE_INLINE void make_geo(const KArgs& A, const Item& it, Geo& G) {
     const int tt = t < it.n ? t : 0;  // unused slots repeat slot 0 (never loaded)
     const uint16_t* rowp;
     if constexpr (MODE == kGateUp) {
-      const int tok = it.shared ? tt : uniform(cview<int32_t>(A.pairs)[it.src_base + tt]) / A.k;
-      rowp = A.x + static_cast<size_t>(tok) * C;
+      rowp = A.x + static_cast<size_t>(it.tok[tt]) * C;
     } else if constexpr (MODE == kDown) {
       rowp = it.shared ? A.act_shared + static_cast<size_t>(tt) * C
                        : A.act + static_cast<size_t>(it.src_base + tt) * C;
@@ -754,25 +929,19 @@ MOE_INLINE bool streamable(const KArgs& A, const Item& it) {
   return it.n <= kMaxTokGroup && it.n < A.dense_threshold;
 }
 
-// Next valid item of this workgroup after item index i (reports invalid descriptors).
-template <int MODE>
-MOE_INLINE int next_item(const KArgs& A, int i, int total, int sh_tiles, int tiles, Item& nx) {
-  int j = i + gridDim.x;
-  while (j < total && !decode_item<MODE>(A, j, sh_tiles, tiles, nx)) {
-    if (threadIdx.x == 0) {
-      atomicOr(&A.err[0], 1);
-      A.err[1] = nx.expert;
-      A.err[2] = MODE;
-    }
-    j += gridDim.x;
+MOE_INLINE void report_invalid(const KArgs& A, const Item& it, int mode) {
+  if (threadIdx.x == 0) {
+    atomicOr(&A.err[0], 1);
+    A.err[1] = it.expert;
+    A.err[2] = mode;
   }
-  return j;
 }
 
 // Process item `it` (index i) and every following item of the same width that is streamable.
-// On return, (i, it) is the first item not processed (i >= total when the list is exhausted).
+// On return, (i, it, ok) describe the first item not processed (i >= total: none left).
 template <int MODE, int Q>
-MOE_INLINE void valu_stream(const KArgs& A, int& i, Item& it, int total, int sh_tiles, int tiles) {
+MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& ok, int total,
+                            int sh_tiles, int tiles) {
   constexpr int D = Ring<Q>::D;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -786,8 +955,9 @@ MOE_INLINE void valu_stream(const KArgs& A, int& i, Item& it, int total, int sh_
   for (int s = 0; s < D; ++s) R.issue(s, cur, s < cur.n ? s : 0);
   while (true) {
     Item next;
-    const int j = next_item<MODE>(A, i, total, sh_tiles, tiles, next);
-    const bool cont = j < total && next.q == Q && streamable<MODE>(A, next);
+    const int j = Qu.nxt;
+    const bool next_ok = j < total && decode_item<MODE>(A, j, sh_tiles, tiles, next);
+    const bool cont = next_ok && next.q == Q && streamable<MODE>(A, next);
     if (cont) make_geo<MODE>(A, next, nxt);
     write_table<Q>(L, lane, wave);
     __syncthreads();
@@ -815,9 +985,10 @@ MOE_INLINE void valu_stream(const KArgs& A, int& i, Item& it, int total, int sh_
     float tot[kMaxTokGroup];
 #pragma unroll
     for (int t = 0; t < kMaxTokGroup; ++t) tot[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
-    reduce_and_store<MODE, kMaxTokGroup>(A, it, 0, it.n, tot);
-    i = j;
+    reduce_and_store<MODE, kMaxTokGroup>(A, it, 0, it.n, tot, Qu);
+    i = queue_advance(A, Qu);
     it = next;
+    ok = next_ok;
     if (!cont) return;
     cur = nxt;
   }
@@ -838,33 +1009,45 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
   const int ssh = MODE == kDown ? A.segs_shared : 1;
   const int srt = MODE == kDown ? A.segs : 1;
   const int total = sh_tiles * ssh + n_routed * tiles * srt;
+  Queue Qu;
+  queue_init(Qu);
+  queue_request(A, Qu);
+  int i = static_cast<int>(blockIdx.x);
   Item it;
-  int i = next_item<MODE>(A, static_cast<int>(blockIdx.x) - static_cast<int>(gridDim.x), total,
-                          sh_tiles, tiles, it);
+  bool ok = i < total && decode_item<MODE>(A, i, sh_tiles, tiles, it);
   while (i < total) {
+    if (!ok) {  // skip an item whose page-table descriptor is invalid
+      report_invalid(A, it, MODE);
+      queue_publish(A, Qu);
+      __syncthreads();
+      i = queue_advance(A, Qu);
+      ok = i < total && decode_item<MODE>(A, i, sh_tiles, tiles, it);
+      continue;
+    }
     if (streamable<MODE>(A, it)) {
       switch (it.q) {
-        case 1: valu_stream<MODE, 1>(A, i, it, total, sh_tiles, tiles); break;
-        case 2: valu_stream<MODE, 2>(A, i, it, total, sh_tiles, tiles); break;
-        case 3: valu_stream<MODE, 3>(A, i, it, total, sh_tiles, tiles); break;
-        case 4: valu_stream<MODE, 4>(A, i, it, total, sh_tiles, tiles); break;
-        case 5: valu_stream<MODE, 5>(A, i, it, total, sh_tiles, tiles); break;
-        case 6: valu_stream<MODE, 6>(A, i, it, total, sh_tiles, tiles); break;
-        case 7: valu_stream<MODE, 7>(A, i, it, total, sh_tiles, tiles); break;
-        default: valu_stream<MODE, 8>(A, i, it, total, sh_tiles, tiles); break;
+        case 1: valu_stream<MODE, 1>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+        case 2: valu_stream<MODE, 2>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+        case 3: valu_stream<MODE, 3>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+        case 4: valu_stream<MODE, 4>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+        case 5: valu_stream<MODE, 5>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+        case 6: valu_stream<MODE, 6>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+        case 7: valu_stream<MODE, 7>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+        default: valu_stream<MODE, 8>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
       }
     } else {
       switch (it.q) {
-        case 1: run_item<MODE, 1>(A, it); break;
-        case 2: run_item<MODE, 2>(A, it); break;
-        case 3: run_item<MODE, 3>(A, it); break;
-        case 4: run_item<MODE, 4>(A, it); break;
-        case 5: run_item<MODE, 5>(A, it); break;
-        case 6: run_item<MODE, 6>(A, it); break;
-        case 7: run_item<MODE, 7>(A, it); break;
-        default: run_item<MODE, 8>(A, it); break;
+        case 1: run_item<MODE, 1>(A, it, Qu); break;
+        case 2: run_item<MODE, 2>(A, it, Qu); break;
+        case 3: run_item<MODE, 3>(A, it, Qu); break;
+        case 4: run_item<MODE, 4>(A, it, Qu); break;
+        case 5: run_item<MODE, 5>(A, it, Qu); break;
+        case 6: run_item<MODE, 6>(A, it, Qu); break;
+        case 7: run_item<MODE, 7>(A, it, Qu); break;
+        default: run_item<MODE, 8>(A, it, Qu); break;
       }
-      i = next_item<MODE>(A, i, total, sh_tiles, tiles, it);
+      i = queue_advance(A, Qu);
+      ok = i < total && decode_item<MODE>(A, i, sh_tiles, tiles, it);
     }
   }
 }

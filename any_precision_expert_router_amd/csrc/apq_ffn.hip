@@ -25,9 +25,12 @@ int launch_apq_ffn(const FfnArgs& a, hipStream_t stream) {
   k.part = a.ws.part; k.part_shared = a.ws.part_shared;
   k.err = a.ws.err;
   k.dense_threshold = a.dense_threshold > 0 ? a.dense_threshold : kDefaultDenseThreshold;
+  k.recs = a.ws.recs;
   const int sh = a.shared ? 1 : 0;
   const int gu_items = sh * (a.I_shared / kGateUpTileRows) + a.E * (a.I / kGateUpTileRows);
+  k.counter = a.ws.counters + kCtrGateUp;
   if (int rc = apq::launch_gate_up(k, gu_items, stream)) return rc;
+  k.counter = a.ws.counters + kCtrDown;
   k.segs = a.ws.segs;
   k.segs_shared = sh ? a.ws.segs_shared : 1;
   const int dn_items = (sh * k.segs_shared + a.E * k.segs) * (a.H / kRowPanel);

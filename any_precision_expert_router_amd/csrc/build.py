@@ -76,6 +76,9 @@ def _check_isa(tmp: str) -> None:
         spills = isa_check.scratch_users(path)
         if spills:
             raise RuntimeError(f"register spills (scratch memory) in {os.path.basename(path)}: {spills}")
+        m0 = isa_check.m0_foreign_uses(path)
+        if m0:
+            raise RuntimeError(f"M0 is used by compiler-generated code in {os.path.basename(path)}: {m0[:5]}")
     if total == 0:
         raise RuntimeError("no DPP instructions found in the device assembly: ISA check did not run")
 

@@ -35,6 +35,35 @@ constexpr int kColChunk = 128;   // columns per 16-byte unit of one plane
 constexpr int kGateUpTileRows = 32;  // gate rows (and as many up rows) per gate_up tile
 constexpr int kWavesPerTile = 4;     // wavefronts sharing one row tile (split over columns)
 
+// ---- per-call expert records ----------------------------------------------------------------
+// What the FFN kernels need about one block pair, gathered once per call by the grouping step so
+// that a work item is decoded with a few scalar loads from one place instead of a chain of
+// dependent loads (active list -> offsets -> page table -> pairs -> gates).  Record 0 is the
+// shared expert, record 1 + a the a-th active routed expert.
+constexpr int kRecTok = 4;   // tokens described in full (the streaming path's group)
+struct alignas(128) ExpertRecord {
+  const uint32_t* planes[2];  // gate_up, down
+  const uint16_t* lut[2];
+  int32_t expert;             // routed expert id, -1 for the shared expert
+  int32_t src_base;           // sorted position of its first pair (0 for the shared expert)
+  int32_t n;                  // tokens routed to it (T for the shared expert)
+  uint8_t q[2];               // committed widths
+  uint8_t ok;                 // both page-table descriptors valid and GPU-resident
+  uint8_t reserved;
+  int32_t tok[kRecTok];       // token rows of its first pairs (activation rows of gate_up)
+  int32_t pair[kRecTok];      // their pair ids t*k + j (partial-sum rows of down)
+  float gate[kRecTok];        // their gate weights
+  int32_t pad[4];
+};
+static_assert(sizeof(ExpertRecord) == 128, "record layout");
+
+// Work counters of the FFN launches (dynamic item fetch), zeroed by the step that writes the
+// records: per launch, kQueues interleaved sub-queues, each counter on its own 128-byte line.
+constexpr int kQueues = 8;
+constexpr int kCounterStride = 32;   // uint32 per counter (128 bytes)
+enum Counter : int { kCtrGateUp = 0, kCtrDown = kQueues * kCounterStride,
+                     kNumCounters = 2 * kQueues * kCounterStride };
+
 // ---- workspace layout (all sections 256-byte aligned) ----------------------------------------
 struct Workspace {
   int32_t* err;          // [64]: device error word + first bad (expert, module)
@@ -49,6 +78,8 @@ struct Workspace {
   float* part;           // fp32 [segs][T*k][H]  gate-scaled expert outputs, pair order
   float* part_shared;    // fp32 [segs_sh][T][H] scaled shared-expert outputs
   int segs, segs_shared; // down column segments (down_segments)
+  ExpertRecord* recs;    // [E + 1]
+  uint32_t* counters;    // [kNumCounters]
   size_t bytes;          // total bytes the layout needs
 };
 Workspace carve_workspace(void* base, int T, int E, int H, int I, int k, int I_shared);
@@ -70,6 +101,28 @@ int launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, fl
                       hipStream_t stream);
 int launch_group_by_expert(const int32_t* ids, int T, int k, int E, int32_t* offsets,
                            int32_t* pairs, int32_t* active, int32_t* n_active, hipStream_t stream);
+
+// Inputs of the record builder (all device pointers; shared may be null).
+struct RecordArgs {
+  const moe_apq_block* table;
+  const moe_apq_block* shared;
+  const float* gates;          // [T*k] gate weights (written by routing in the same launch or before)
+  int E, H, I, I_shared, T, k;
+  ExpertRecord* recs;
+  uint32_t* counters;
+};
+// Routing, grouping and the records in one single-workgroup launch (small batches).
+constexpr int kFusedRouteMaxT = 16;   // one token per wavefront of the fused workgroup
+constexpr int kFusedRouteMaxPairs = kFusedRouteMaxT * MOE_MAX_TOPK;
+int launch_route_group_records(const float* logits, int32_t* ids, float* gates, int32_t* offsets,
+                               int32_t* pairs, int32_t* active, int32_t* n_active,
+                               const RecordArgs& r, hipStream_t stream);
+// Grouping then records (large batches, after launch_route_topk).
+int launch_group_records(const int32_t* ids, int32_t* offsets, int32_t* pairs, int32_t* active,
+                         int32_t* n_active, const RecordArgs& r, hipStream_t stream);
+// Records only, from routing arrays the caller computed (moe_apq_ffn).
+int launch_records(const int32_t* offsets, const int32_t* pairs, const int32_t* active,
+                   const int32_t* n_active, const RecordArgs& r, hipStream_t stream);
 
 struct FfnArgs {
   const moe_apq_block* table;  // device [E][2]

@@ -12,6 +12,10 @@ rules checked, each as a minimum number of wait states between two instructions:
 and branches into its block) and reports each gap that is too short.
 
 `scratch_users` reports kernels that use scratch memory (register spills).
+
+`m0_foreign_uses` reports instructions other than "s_mov_b32 m0, ..." that name M0: the
+hand-written buffer-to-LDS loads set M0 without telling the compiler, which is only safe while
+nothing else in the kernel reads it.
 """
 from __future__ import annotations
 
@@ -167,6 +171,14 @@ def scratch_users(path: str):
             m = re.match(r"\s*\.amdhsa_private_segment_fixed_size\s+(\d+)", line)
             if m and name and int(m.group(1)) > 0:
                 out.append(f"{name} ({m.group(1)} bytes)")
+    return out
+
+
+def m0_foreign_uses(path: str):
+    out = []
+    for kind, t in _program(path):
+        if kind == "inst" and re.search(r"\bm0\b", t) and not t.startswith("s_mov_b32 m0,"):
+            out.append(t)
     return out
 
 

@@ -34,15 +34,30 @@ __device__ __forceinline__ float key_logit(uint64_t key) {
   return __uint_as_float(u);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_dpp(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v), CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v >> 32), CTRL, 0xf, 0xf, false);
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Wavefront maximum of a 64-bit key, returned uniform: DPP butterflies inside each 16-lane row
+// (quad swaps, then half-row and row mirrors), then the four row maxima through scalar registers.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 64);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 64);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = max_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = max_dpp<0x141>(v);  // row_half_mirror
+  v = max_dpp<0x140>(v);  // row_mirror
+  const uint64_t a = readlane64(v, 0), b = readlane64(v, 16), c = readlane64(v, 32), d = readlane64(v, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -51,14 +66,12 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// One wavefront routes token t: each lane holds PER_LANE candidate keys; k rounds of the
+// wavefront maximum select the experts in order; the gates are the softmax of the k logits.
 template <int PER_LANE>
-__global__ __launch_bounds__(64 * kRouteWaves) void route_topk_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ gates) {
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int32_t* ids_out,
+                                            float* gates_out, int32_t* ids_copy, float* gates_copy) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + static_cast<size_t>(t) * E;
   uint64_t key[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
@@ -76,83 +89,226 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_topk_kernel(
       if (key[i] == win) key[i] = 0ull;  // unique: ids differ
     if (lane == j) mine = win;
   }
-  const float l0 = key_logit(__shfl(mine, 0, 64));
+  const float l0 = key_logit(readlane64(mine, 0));
   const float z = lane < k ? expf(key_logit(mine) - l0) : 0.0f;
   const float s = wave_sum_f32(z);
   if (lane < k) {
-    const size_t o = static_cast<size_t>(t) * k + lane;
-    ids[o] = static_cast<int32_t>(~static_cast<uint32_t>(mine));
-    gates[o] = z / s;
+    const int32_t id = static_cast<int32_t>(~static_cast<uint32_t>(mine));
+    ids_out[lane] = id;
+    gates_out[lane] = z / s;
+    if (ids_copy) ids_copy[lane] = id;
+    if (gates_copy) gates_copy[lane] = z / s;
   }
+}
+
+template <int PER_LANE>
+__global__ __launch_bounds__(64 * kRouteWaves) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ gates) {
+  const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const size_t o = static_cast<size_t>(t) * k;
+  route_token<PER_LANE>(logits + static_cast<size_t>(t) * E, E, k, ids + o, gates + o, nullptr, nullptr);
 }
 
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupMapBytes = 16384;  // LDS token x expert slot map per chunk
 
-__global__ __launch_bounds__(kGroupThreads) void group_by_expert_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ pairs, int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
-  __shared__ int32_t count[MOE_MAX_EXPERTS];
-  __shared__ int32_t wave_tot[2][kGroupThreads / 64];
-  __shared__ uint8_t slot_map[kGroupMapBytes];
+struct GroupSmem {
+  int32_t count[MOE_MAX_EXPERTS];
+  int32_t wave_tot[2][kGroupThreads / 64];
+  uint8_t slot_map[kGroupMapBytes];
+  int32_t offsets[MOE_MAX_EXPERTS + 1];  // LDS copies of the grouping results for the records
+  int32_t active[MOE_MAX_EXPERTS];
+  int32_t n_active;
+};
+
+// Stable grouping by one workgroup of kGroupThreads threads.  `ids` may have been written by this
+// workgroup before a barrier.
+__device__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ pairs, int32_t* __restrict__ active,
+                           int32_t* __restrict__ n_active, GroupSmem& sm, int32_t* pairs_lds) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int TK = T * k;
 
-  for (int e = tid; e < E; e += kGroupThreads) count[e] = 0;
+  for (int e = tid; e < E; e += kGroupThreads) sm.count[e] = 0;
   __syncthreads();
-  for (int p = tid; p < TK; p += kGroupThreads) atomicAdd(&count[ids[p]], 1);
+  for (int p = tid; p < TK; p += kGroupThreads) atomicAdd(&sm.count[ids[p]], 1);
   __syncthreads();
 
   // exclusive scans of count[e] and of (count[e] > 0), one thread per expert (E <= 1024)
-  const int c = tid < E ? count[tid] : 0;
+  const int c = tid < E ? sm.count[tid] : 0;
   int a = c, f = c > 0 ? 1 : 0;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int a2 = __shfl_up(a, off, 64), f2 = __shfl_up(f, off, 64);
     if (lane >= off) { a += a2; f += f2; }
   }
-  if (lane == 63) { wave_tot[0][wave] = a; wave_tot[1][wave] = f; }
+  if (lane == 63) { sm.wave_tot[0][wave] = a; sm.wave_tot[1][wave] = f; }
   __syncthreads();
   int base_a = 0, base_f = 0;
-  for (int w = 0; w < wave; ++w) { base_a += wave_tot[0][w]; base_f += wave_tot[1][w]; }
+  for (int w = 0; w < wave; ++w) { base_a += sm.wave_tot[0][w]; base_f += sm.wave_tot[1][w]; }
   const int excl = base_a + a - c;
   const int act_pos = base_f + f - (c > 0 ? 1 : 0);
   if (tid < E) {
     offsets[tid] = excl;
-    if (c > 0) active[act_pos] = tid;
+    sm.offsets[tid] = excl;
+    if (c > 0) {
+      active[act_pos] = tid;
+      sm.active[act_pos] = tid;
+    }
   }
   if (tid == E - 1) {
     offsets[E] = excl + c;
+    sm.offsets[E] = excl + c;
     n_active[0] = act_pos + (c > 0 ? 1 : 0);
+    sm.n_active = act_pos + (c > 0 ? 1 : 0);
   }
   __syncthreads();
   // -1 padding after the active list
   int n_act = 0;
-  for (int w = 0; w < kGroupThreads / 64; ++w) n_act += wave_tot[1][w];
+  for (int w = 0; w < kGroupThreads / 64; ++w) n_act += sm.wave_tot[1][w];
   for (int e = tid; e < E; e += kGroupThreads)
     if (e >= n_act) active[e] = -1;
 
-  // stable placement, chunk by chunk over tokens
+  // stable placement, chunk by chunk over tokens: because the k experts of one token are
+  // distinct, a pair's rank inside its expert is the number of earlier tokens that picked it
   int cursor = excl;
   const int chunk = kGroupMapBytes / E > 0 ? kGroupMapBytes / E : 1;
   for (int t0 = 0; t0 < T; t0 += chunk) {
     const int tn = min(chunk, T - t0);
-    for (int i = tid; i < tn * E; i += kGroupThreads) slot_map[i] = 0;
+    for (int i = tid; i < tn * E; i += kGroupThreads) sm.slot_map[i] = 0;
     __syncthreads();
     for (int i = tid; i < tn * k; i += kGroupThreads) {
       const int tt = i / k, j = i - tt * k;
-      slot_map[tt * E + ids[(t0 + tt) * k + j]] = static_cast<uint8_t>(j + 1);
+      sm.slot_map[tt * E + ids[(t0 + tt) * k + j]] = static_cast<uint8_t>(j + 1);
     }
     __syncthreads();
     if (tid < E && c > 0) {
       for (int tt = 0; tt < tn; ++tt) {
-        const int s = slot_map[tt * E + tid];
-        if (s) pairs[cursor++] = (t0 + tt) * k + (s - 1);
+        const int s = sm.slot_map[tt * E + tid];
+        if (s) {
+          const int p = (t0 + tt) * k + (s - 1);
+          if (pairs_lds) pairs_lds[cursor] = p;
+          pairs[cursor++] = p;
+        }
       }
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_by_expert_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ pairs, int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  __shared__ GroupSmem sm;
+  group_body(ids, T, k, E, offsets, pairs, active, n_active, sm, nullptr);
+}
+
+__device__ __forceinline__ bool block_valid(const moe_apq_block& b, int rows, int cols) {
+  const uintptr_t align = reinterpret_cast<uintptr_t>(b.planes) | reinterpret_cast<uintptr_t>(b.lut);
+  return b.planes != nullptr && b.lut != nullptr && (align & 15) == 0 && b.rows == rows &&
+         b.cols == cols && b.q >= 1 && b.q <= 8 && b.state == MOE_PAGE_GPU;
+}
+
+__device__ __forceinline__ void fill_record(ExpertRecord& rec, const moe_apq_block& gu,
+                                            const moe_apq_block& dn, int inter, const RecordArgs& r) {
+  rec.planes[0] = gu.planes;
+  rec.planes[1] = dn.planes;
+  rec.lut[0] = gu.lut;
+  rec.lut[1] = dn.lut;
+  rec.q[0] = gu.q;
+  rec.q[1] = dn.q;
+  rec.ok = block_valid(gu, 2 * inter, r.H) && block_valid(dn, r.H, inter) ? 1 : 0;
+  rec.reserved = 0;
+}
+
+// Records of the shared expert and of every active routed expert, and zeroed work counters.
+// The grouping comes from this workgroup's LDS copies (after a barrier); pairs and gates from
+// LDS when the routing ran in this workgroup, else from global memory.
+__device__ void records_body(const GroupSmem& sm, const int32_t* pairs, const float* gates,
+                             const RecordArgs& r) {
+  const int tid = threadIdx.x;
+  const int n_act = sm.n_active;
+  for (int a = tid; a < n_act; a += blockDim.x) {
+    const int e = sm.active[a];
+    ExpertRecord rec;
+    fill_record(rec, r.table[2 * e], r.table[2 * e + 1], r.I, r);
+    rec.expert = e;
+    rec.src_base = sm.offsets[e];
+    rec.n = sm.offsets[e + 1] - rec.src_base;
+#pragma unroll
+    for (int t = 0; t < kRecTok; ++t) {
+      const int p = t < rec.n ? pairs[rec.src_base + t] : 0;
+      rec.pair[t] = p;
+      rec.tok[t] = p / r.k;
+      rec.gate[t] = t < rec.n ? gates[p] : 0.0f;
+    }
+    r.recs[1 + a] = rec;
+  }
+  if (tid == 0) {
+    ExpertRecord rec{};
+    if (r.shared) {
+      fill_record(rec, r.shared[0], r.shared[1], r.I_shared, r);
+    } else {
+      rec.ok = 0;
+    }
+    rec.expert = -1;
+    rec.src_base = 0;
+    rec.n = r.T;
+#pragma unroll
+    for (int t = 0; t < kRecTok; ++t) {
+      rec.tok[t] = t < r.T ? t : 0;
+      rec.pair[t] = rec.tok[t];
+      rec.gate[t] = 1.0f;
+    }
+    r.recs[0] = rec;
+  }
+  for (int c = tid; c < kNumCounters; c += blockDim.x) r.counters[c] = 0u;
+}
+
+// Routing of up to kFusedRouteMaxT tokens by the 16 wavefronts of one workgroup, then grouping
+// and records, without leaving the workgroup.
+template <int PER_LANE>
+__global__ __launch_bounds__(kGroupThreads) void route_group_records_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ gates, int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, RecordArgs r) {
+  __shared__ GroupSmem sm;
+  __shared__ int32_t s_ids[kFusedRouteMaxPairs];
+  __shared__ float s_gates[kFusedRouteMaxPairs];
+  __shared__ int32_t s_pairs[kFusedRouteMaxPairs];
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kGroupThreads / 64) {
+    const size_t o = static_cast<size_t>(t) * k;
+    route_token<PER_LANE>(logits + static_cast<size_t>(t) * E, E, k, ids + o, gates + o, s_ids + o,
+                          s_gates + o);
+  }
+  __syncthreads();
+  group_body(s_ids, T, k, E, offsets, pairs, active, n_active, sm, s_pairs);
+  __syncthreads();
+  records_body(sm, s_pairs, s_gates, r);
+}
+
+__global__ __launch_bounds__(kGroupThreads) void group_records_kernel(
+    const int32_t* __restrict__ ids, int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, RecordArgs r) {
+  __shared__ GroupSmem sm;
+  group_body(ids, r.T, r.k, r.E, offsets, pairs, active, n_active, sm, nullptr);
+  __syncthreads();
+  records_body(sm, pairs, r.gates, r);
+}
+
+__global__ __launch_bounds__(kGroupThreads) void records_kernel(
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ pairs,
+    const int32_t* __restrict__ active, const int32_t* __restrict__ n_active, RecordArgs r) {
+  __shared__ GroupSmem sm;
+  for (int e = threadIdx.x; e <= r.E; e += blockDim.x) sm.offsets[e] = offsets[e];
+  for (int e = threadIdx.x; e < r.E; e += blockDim.x) sm.active[e] = active[e];
+  if (threadIdx.x == 0) sm.n_active = n_active[0];
+  __syncthreads();
+  records_body(sm, pairs, r.gates, r);
 }
 
 }  // namespace
@@ -181,6 +337,37 @@ int launch_group_by_expert(const int32_t* ids, int T, int k, int E, int32_t* off
   hipLaunchKernelGGL(group_by_expert_kernel, dim3(1), dim3(kGroupThreads), 0, stream, ids, T, k,
                      E, offsets, pairs, active, n_active);
   return check_launch("group_by_expert");
+}
+
+int launch_route_group_records(const float* logits, int32_t* ids, float* gates, int32_t* offsets,
+                               int32_t* pairs, int32_t* active, int32_t* n_active,
+                               const RecordArgs& r, hipStream_t stream) {
+  ProfileScope prof("route_group", stream);
+#define MOE_RG_CASE(PL)                                                                          \
+  hipLaunchKernelGGL(route_group_records_kernel<PL>, dim3(1), dim3(kGroupThreads), 0, stream,     \
+                     logits, r.T, r.E, r.k, ids, gates, offsets, pairs, active, n_active, r)
+  if (r.E <= 64) MOE_RG_CASE(1);
+  else if (r.E <= 128) MOE_RG_CASE(2);
+  else if (r.E <= 256) MOE_RG_CASE(4);
+  else if (r.E <= 512) MOE_RG_CASE(8);
+  else MOE_RG_CASE(16);
+#undef MOE_RG_CASE
+  return check_launch("route_group");
+}
+
+int launch_group_records(const int32_t* ids, int32_t* offsets, int32_t* pairs, int32_t* active,
+                         int32_t* n_active, const RecordArgs& r, hipStream_t stream) {
+  ProfileScope prof("group_by_expert", stream);
+  hipLaunchKernelGGL(group_records_kernel, dim3(1), dim3(kGroupThreads), 0, stream, ids, offsets,
+                     pairs, active, n_active, r);
+  return check_launch("group_by_expert");
+}
+
+int launch_records(const int32_t* offsets, const int32_t* pairs, const int32_t* active,
+                   const int32_t* n_active, const RecordArgs& r, hipStream_t stream) {
+  ProfileScope prof("expert_records", stream);
+  hipLaunchKernelGGL(records_kernel, dim3(1), dim3(256), 0, stream, offsets, pairs, active, n_active, r);
+  return check_launch("expert_records");
 }
 
 }  // namespace moeapq
