@@ -29,7 +29,8 @@ GATE_UP, DOWN = 0, 1
 EXPORTED = (
     "moe_route_topk", "moe_group_by_expert", "moe_apq_ffn", "moe_layer_forward",
     "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
-    "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_last_error",
+    "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_hbm_read_probe",
+    "moe_last_error",
 )
 
 
@@ -76,6 +77,7 @@ def _load():
         "moe_check_device_error": ([P, Z, S], I),
         "moe_profile_start": ([], I),
         "moe_profile_stop": ([I, P, P, P], I),
+        "moe_hbm_read_probe": ([P, Z, P, S], I),
         "moe_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -181,6 +183,12 @@ def moe_apq_decode_indices(block: ApqBlock, idx_out, stream=None) -> None:
 def moe_check_device_error(workspace, stream=None) -> None:
     _check("moe_check_device_error", _lib.moe_check_device_error(_ptr(workspace), workspace.numel(),
                                                                  _stream(stream)))
+
+
+def moe_hbm_read_probe(buf, sink, stream=None) -> None:
+    """Stream-read `buf` (device tensor, size a multiple of 1 KiB) once; XOR of the data into sink."""
+    _check("moe_hbm_read_probe", _lib.moe_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
+                                                         _ptr(sink), _stream(stream)))
 
 
 def moe_profile_start() -> None:

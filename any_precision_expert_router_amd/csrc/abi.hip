@@ -291,6 +291,15 @@ int moe_check_device_error(void* workspace, size_t ws_bytes, void* stream) {
                    word[1], word[2] == 0 ? "gate_up" : "down");
 }
 
+int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  clear_error();
+  if (!buf || !sink) return set_error(MOE_EINVAL, "NULL pointer argument");
+  if (bytes == 0 || bytes % 1024 || bytes > (size_t(1) << 40))
+    return set_error(MOE_EINVAL, "bytes must be a positive multiple of 1024, at most 2^40");
+  if (reinterpret_cast<uintptr_t>(buf) & 15) return set_error(MOE_EINVAL, "buf must be 16-byte aligned");
+  return launch_hbm_read_probe(buf, bytes, sink, as_stream(stream));
+}
+
 int moe_profile_start(void) {
   clear_error();
   for (auto& r : g_prof.recs) {

@@ -16,7 +16,8 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoe_apq.so"
-SOURCES = ["apq_gate_up.hip", "apq_down.hip", "apq_plain.hip", "abi.hip", "route.hip", "apq_ffn.hip", "pack.cpp"]
+SOURCES = ["apq_gate_up.hip", "apq_down.hip", "apq_plain.hip", "abi.hip", "route.hip", "apq_ffn.hip",
+           "probe.hip", "pack.cpp"]
 ARCH = os.environ.get("MOE_APQ_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

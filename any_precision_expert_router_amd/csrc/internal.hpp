@@ -146,5 +146,6 @@ int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y
 // Tiles with at least this many tokens use the matrix-core (MFMA) path by default.
 constexpr int kDefaultDenseThreshold = 5;
 int launch_decode_indices(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
+int launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace moeapq

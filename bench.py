@@ -138,6 +138,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB: the known-size "
                          "dispatch that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -224,6 +225,57 @@ def main():
     log(f"[bench] {args.steps} steps: wall {wall_ms:.2f} ms, events {ev_ms:.2f} ms "
         f"-> {1e3 * ms_per_step:.2f} us/layer (events {1e3 * ev_ms / args.steps:.2f})")
 
+    # the same steps replayed from HIP graphs (one captured call per weight copy); every replay
+    # must reproduce the eager output bit for bit
+    graph = None
+    if not args.no_graph:
+        y_eager = y.clone()
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for c in copies:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    apq.moe_layer_forward(logits, x, shape.E, shape.H, shape.I, shape.k, c.table, y, ws,
+                                          shared=c.shared, I_shared=shape.I_shared, stream=side)
+                graphs.append(g)
+        stream.wait_stream(side)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_us = 1e3 * g0.elapsed_time(g1) / args.steps
+        same = bool(torch.equal(y, y_eager))
+        log(f"[bench] graph replay: {graph_us:.2f} us/layer, output identical to eager: {same}")
+        assert same, "graph replay output differs from the eager call"
+        graph = {"us_per_layer": round(graph_us, 2),
+                 "GBs": round(weight_bytes / (graph_us * 1e-6) / 1e9, 1)}
+        del graphs
+
+    # achievable streaming-read rate of this device (the library's read probe over 2 GiB)
+    probe = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        apq.moe_hbm_read_probe(probe, sink)
+    torch.cuda.synchronize()
+    p0 = torch.cuda.Event(enable_timing=True)
+    p1 = torch.cuda.Event(enable_timing=True)
+    p0.record()
+    for _ in range(5):
+        apq.moe_hbm_read_probe(probe, sink)
+    p1.record()
+    torch.cuda.synchronize()
+    read_ceiling = probe.numel() / (p0.elapsed_time(p1) * 1e-3 / 5) / 1e9
+    del probe
+    log(f"[bench] streaming-read ceiling: {read_ceiling:.1f} GB/s")
+
     # per-kernel durations: the same steps again with every library launch bracketed by events
     apq.moe_profile_start()
     for i in range(args.steps):
@@ -267,6 +319,11 @@ def main():
                    "weight_bytes_per_call": int(weight_bytes), "plane_bytes": int(planes_b),
                    "lut_bytes": int(lut_b), "weight_copies": n_copies},
         "per_kernel_us": {k: round(v["avg_us"], 3) for k, v in per_kernel.items()},
+        "hbm_read_ceiling_GBs": round(read_ceiling, 1),
+        "pct_read_ceiling": round(100 * value / read_ceiling, 2),
+        "timing": "eager moe_layer_forward calls (headline); graph_replay below replays the same call "
+                  "from captured HIP graphs",
+        "graph_replay": graph,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -203,6 +203,17 @@ int moe_profile_start(void);
 int moe_profile_stop(int max_kernels, char* names_out, double* total_ms_out,
                      int32_t* launches_out);
 
+/*
+ * Diagnostic: read `bytes` of device memory at `buf` once, with the access pattern that streams
+ * fastest on this device (every wavefront reads one contiguous run in 1-KiB non-temporal loads,
+ * 16 in flight), and XOR every 32-bit word of it into `*sink` (device, 4 bytes, stream-ordered
+ * atomic: the caller clears it first to read the XOR of the buffer).  bytes must be a positive
+ * multiple of 1024, at most 2^40, and buf 16-byte aligned; otherwise MOE_EINVAL and nothing is
+ * launched.  Timing this call gives the achievable HBM read rate that the layer's bandwidth is
+ * compared with.
+ */
+int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -297,3 +297,46 @@ def test_invalid_descriptor_is_reported_not_read():
         apq.moe_check_device_error(ws)
     assert ei.value.code == apq.MOE_EDEVICE
     apq.moe_check_device_error(ws)    # cleared by the read
+
+
+def test_layer_replays_from_a_hip_graph():
+    """moe_layer_forward issues no host synchronisation and no memset, so it can be captured;
+    every replay (with other eager work between them) equals the eager call bit for bit."""
+    shape = wl.TINY.replace(H=256, E=8, I=256, k=2, T=12, I_shared=256, q_shared=8, name="graph")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    y_ref, _ = _run_layer(shape, inputs, dl)
+    T = shape.T
+    lg, x = _t(inputs.logits), _t(inputs.x)
+    y = torch.zeros((T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(T, shape.E, shape.H, shape.I, shape.k, shape.I_shared),
+                     dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            apq.moe_layer_forward(lg, x, shape.E, shape.H, shape.I, shape.k, dl.table, y, ws,
+                                  shared=dl.shared, I_shared=shape.I_shared, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    for r in range(3):
+        y.zero_()
+        ws.fill_(0x5A)          # the replay must not depend on leftovers in its workspace
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.float().cpu().numpy().astype(np.float64), y_ref)
+        _run_layer(shape, inputs, dl)   # eager work between replays
+
+
+@pytest.mark.parametrize("kib", [1, 37, 4096 + 3])
+def test_hbm_read_probe_reads_every_word_once(kib):
+    """The read-ceiling probe folds each 32-bit word into its sink exactly once: the sink equals
+    the XOR of the buffer computed on the host (sizes below, at and above one unit per wavefront)."""
+    g = torch.Generator().manual_seed(kib)
+    host = torch.randint(-2**31, 2**31 - 1, (kib * 256,), dtype=torch.int64, generator=g).to(torch.int32)
+    buf = host.to(DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    apq.moe_hbm_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
