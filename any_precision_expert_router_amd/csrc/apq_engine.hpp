@@ -133,8 +133,10 @@ MOE_INLINE uint32_t word_of(const u32x4& v, int jw) {
 constexpr int kLutRegs = 8;  // 16-byte LUT registers one thread prefetches for an item
 
 // Depth of the per-wavefront ring of in-flight 128-column chunks (all q planes of a chunk).
+// Two chunks per wavefront, with eight wavefronts per CU, keep 16 chunks per CU in flight; a
+// deeper ring measured slower (it costs 32 VGPRs per slot and doubles the unrolled loop body).
 template <int Q>
-constexpr int ring_depth() { return Q <= 4 ? 4 : (Q == 5 ? 3 : 2); }
+constexpr int ring_depth() { return 2; }
 
 struct Item {
   const uint32_t* planes;
@@ -178,41 +180,49 @@ struct KArgs {
 };
 
 // Work queue of a workgroup.  Its first two items are blockIdx.x and blockIdx.x + gridDim.x;
-// the later ones come from its sub-queue's counter, requested by thread 0 one item ahead and published to the workgroup through LDS at the current item's
-// reduction barrier, so the atomic's latency hides behind a whole item.  Without a counter the
-// queue is static round-robin.
+// the later ones come from its sub-queue's counter, requested by thread 0 one item ahead and
+// published to the workgroup through LDS at the current item's reduction barrier, so the
+// atomic's latency hides behind a whole item.  Without a counter the queue is static
+// round-robin.  Everything the publish step needs is computed once here, so that step reads no
+// memory (a reload of a kernel argument there costs a scalar-load round trip per item).
 struct Queue {
   int nxt;            // the item after the current one (uniform)
-  int sub, nsub;      // this workgroup's sub-queue and the number of sub-queues
+  int base, stride;   // dynamic: item = base + stride * counter value; static: nxt + stride
+  bool dynamic;       // a counter exists
+  uint32_t* counter;  // this workgroup's sub-queue counter (thread 0 only)
   uint32_t pending;   // thread 0: counter value fetched for the item after nxt
 };
 
 // The dynamic items (from 2 * gridDim.x on) are dealt to min(kQueues, gridDim.x) interleaved
 // sub-queues, each with its own counter, so that no single address takes every fetch.
-MOE_INLINE void queue_init(Queue& Qu) {
-  Qu.nxt = static_cast<int>(blockIdx.x + gridDim.x);
-  Qu.nsub = min(kQueues, static_cast<int>(gridDim.x));
-  Qu.sub = static_cast<int>(blockIdx.x) % Qu.nsub;
+MOE_INLINE void queue_init(const KArgs& A, Queue& Qu) {
+  const int grid = static_cast<int>(gridDim.x);
+  const int nsub = min(kQueues, grid);
+  const int sub = static_cast<int>(blockIdx.x) % nsub;
+  Qu.nxt = static_cast<int>(blockIdx.x) + grid;
+  Qu.dynamic = A.counter != nullptr;
+  Qu.base = Qu.dynamic ? 2 * grid + sub : 0;
+  Qu.stride = Qu.dynamic ? nsub : grid;
+  Qu.counter = Qu.dynamic ? A.counter + sub * kCounterStride : nullptr;
   Qu.pending = 0;
 }
-MOE_INLINE void queue_request(const KArgs& A, Queue& Qu) {
-  if (A.counter && threadIdx.x == 0) Qu.pending = atomicAdd(A.counter + Qu.sub * kCounterStride, 1u);
+MOE_INLINE void queue_request(Queue& Qu) {
+  if (Qu.dynamic && threadIdx.x == 0) Qu.pending = atomicAdd(Qu.counter, 1u);
 }
 // Before the barrier: thread 0 publishes the item after nxt.
-MOE_INLINE void queue_publish(const KArgs& A, const Queue& Qu) {
+MOE_INLINE void queue_publish(const Queue& Qu) {
   if (threadIdx.x == 0) {
-    const int after = A.counter ? 2 * static_cast<int>(gridDim.x) + Qu.sub + Qu.nsub * static_cast<int>(Qu.pending)
-                                : Qu.nxt + static_cast<int>(gridDim.x);
-    *reinterpret_cast<volatile int*>(reinterpret_cast<char*>(g_lds) + kQueueBase) = after;
+    const int after = Qu.dynamic ? Qu.base + Qu.stride * static_cast<int>(Qu.pending) : Qu.nxt + Qu.stride;
+    g_lds[kQueueBase / 4] = static_cast<uint32_t>(after);
   }
 }
 // After the barrier: every thread reads it, the queue moves one item on and requests the next.
 // Returns the item that becomes current.
-MOE_INLINE int queue_advance(const KArgs& A, Queue& Qu) {
-  const int after = uniform(*reinterpret_cast<volatile int*>(reinterpret_cast<char*>(g_lds) + kQueueBase));
+MOE_INLINE int queue_advance(Queue& Qu) {
+  const int after = uniform(static_cast<int>(g_lds[kQueueBase / 4]));
   const int cur = Qu.nxt;
   Qu.nxt = after;
-  queue_request(A, Qu);
+  queue_request(Qu);
   return cur;
 }
 
@@ -369,7 +379,7 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
 #pragma unroll
     for (int t = 0; t < NT; ++t) red[((wave - 1) * kMaxTokGroup + t) * 64 + lane] = acc[t];
   }
-  queue_publish(A, Qu);
+  queue_publish(Qu);
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
@@ -409,12 +419,101 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
 }
 
 // Item i of the launch's list: shared-expert tiles first (they carry every token), then the
-// routed experts' tiles, each described by its expert record.  Returns false if the record says
-// a page-table descriptor is invalid.
+// routed experts' tiles, each described by its expert record.  Decoding is split in three steps
+// so that a caller can issue the record's scalar loads early and use them later: locate_item
+// (index arithmetic only), load_record (the loads) and fill_item (the uses).
+struct ItemLoc {
+  int slot;   // record slot: 0 = shared expert, 1 + a = a-th active routed expert
+  int nseg;   // column segments of the block's rows
+  int inter;  // intermediate size of the expert
+};
+
+template <int MODE>
+MOE_INLINE ItemLoc locate_item(const KArgs& A, int i, int sh_tiles, int tiles, Item& it) {
+  constexpr int kTileRows = MODE == kGateUp ? kGateUpTileRows : kRowPanel;
+  // segments exist for down items only (the SiLU epilogue of gate_up needs whole rows)
+  const int ssh = MODE == kDown ? A.segs_shared : 1;
+  const int srt = MODE == kDown ? A.segs : 1;
+  ItemLoc loc;
+  if (i < sh_tiles * ssh) {
+    loc.slot = 0;
+    it.shared = true;
+    it.r0 = (i / ssh) * kTileRows;
+    it.seg = i - (i / ssh) * ssh;
+    loc.nseg = ssh;
+    loc.inter = A.I_shared;
+  } else {
+    const int r = i - sh_tiles * ssh;
+    const int per = tiles * srt;
+    const int a = r / per, rem = r - a * per, tile = rem / srt;
+    loc.slot = 1 + a;
+    it.shared = false;
+    it.r0 = tile * kTileRows;
+    it.seg = rem - tile * srt;
+    loc.nseg = srt;
+    loc.inter = A.I;
+  }
+  return loc;
+}
+
+// The fields of an expert record that an item uses, held in registers.
+struct RecFields {
+  const uint32_t* planes;
+  const uint16_t* lut;
+  int q, expert, src_base, n;
+  int tok[kRecTok], pair[kRecTok];
+  float gate[kRecTok];
+  bool ok;
+};
+
+template <int MODE>
+MOE_INLINE RecFields load_record(const KArgs& A, int slot) {
+  const AS_CONST ExpertRecord& rec = cview<ExpertRecord>(A.recs)[slot];
+  RecFields f;
+  f.planes = rec.planes[MODE];
+  f.lut = rec.lut[MODE];
+  const uint32_t meta = rec.meta;
+  f.q = record_q(meta, MODE);
+  f.expert = rec.expert;
+  f.src_base = rec.src_base;
+  f.n = rec.n;
+#pragma unroll
+  for (int t = 0; t < kRecTok; ++t) {
+    f.tok[t] = rec.tok[t];
+    f.pair[t] = rec.pair[t];
+    f.gate[t] = rec.gate[t];
+  }
+  f.ok = record_ok(meta);
+  return f;
+}
+
+// Returns false if the record says a page-table descriptor is invalid.
+template <int MODE>
+MOE_INLINE bool fill_item(const KArgs& A, const RecFields& f, const ItemLoc& loc, Item& it) {
+  it.planes = f.planes;
+  it.lut = f.lut;
+  it.q = f.q;
+  it.expert = f.expert;
+  it.src_base = f.src_base;
+  it.n = f.n;
+#pragma unroll
+  for (int t = 0; t < kRecTok; ++t) {
+    it.tok[t] = f.tok[t];
+    it.pair[t] = f.pair[t];
+    it.gate[t] = f.gate[t];
+  }
+  it.rows = MODE == kGateUp ? 2 * loc.inter : A.H;
+  it.cols = MODE == kGateUp ? A.H : loc.inter;
+  it.row_hi = MODE == kGateUp ? loc.inter + it.r0 : it.r0 + 32;
+  if (!f.ok) return false;
+  const int nc4 = it.cols / kColChunk;
+  it.c0 = uniform(it.seg * nc4 / loc.nseg);
+  it.nc = uniform((it.seg + 1) * nc4 / loc.nseg) - it.c0;
+  return true;
+}
+
 template <int MODE>
 MOE_INLINE bool decode_item(const KArgs& A, int i, int sh_tiles, int tiles, Item& it) {
-  constexpr int kTileRows = MODE == kGateUp ? kGateUpTileRows : kRowPanel;
-  int inter = 0;
   it.expert = -1;
   if constexpr (MODE == kPlain) {
     const moe_apq_block& b = A.plain;
@@ -436,51 +535,12 @@ MOE_INLINE bool decode_item(const KArgs& A, int i, int sh_tiles, int tiles, Item
       it.pair[t] = t;
       it.gate[t] = 1.0f;
     }
+    it.row_hi = it.r0 + 32;
+    return true;
   } else {
-    // segments exist for down items only (the SiLU epilogue of gate_up needs whole rows)
-    const int ssh = MODE == kDown ? A.segs_shared : 1;
-    const int srt = MODE == kDown ? A.segs : 1;
-    int nseg, slot;
-    if (i < sh_tiles * ssh) {
-      slot = 0;
-      it.shared = true;
-      it.r0 = (i / ssh) * kTileRows;
-      it.seg = i - (i / ssh) * ssh;
-      nseg = ssh;
-      inter = A.I_shared;
-    } else {
-      const int r = i - sh_tiles * ssh;
-      const int per = tiles * srt;
-      const int a = r / per, rem = r - a * per, tile = rem / srt;
-      slot = 1 + a;
-      it.shared = false;
-      it.r0 = tile * kTileRows;
-      it.seg = rem - tile * srt;
-      nseg = srt;
-      inter = A.I;
-    }
-    const AS_CONST ExpertRecord& rec = cview<ExpertRecord>(A.recs)[slot];
-    it.planes = rec.planes[MODE];
-    it.lut = rec.lut[MODE];
-    it.q = rec.q[MODE];
-    it.expert = rec.expert;
-    it.src_base = rec.src_base;
-    it.n = rec.n;
-#pragma unroll
-    for (int t = 0; t < kRecTok; ++t) {
-      it.tok[t] = rec.tok[t];
-      it.pair[t] = rec.pair[t];
-      it.gate[t] = rec.gate[t];
-    }
-    it.rows = MODE == kGateUp ? 2 * inter : A.H;
-    it.cols = MODE == kGateUp ? A.H : inter;
-    if (!rec.ok) return false;
-    const int nc4 = it.cols / kColChunk;
-    it.c0 = uniform(it.seg * nc4 / nseg);
-    it.nc = uniform((it.seg + 1) * nc4 / nseg) - it.c0;
+    const ItemLoc loc = locate_item<MODE>(A, i, sh_tiles, tiles, it);
+    return fill_item<MODE>(A, load_record<MODE>(A, loc.slot), loc, it);
   }
-  it.row_hi = MODE == kGateUp ? inter + it.r0 : it.r0 + 32;
-  return true;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -744,7 +804,7 @@ MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, i
       mine[(16 + i) * 64 + lane] = hi[i];
     }
   }
-  if (Qu) queue_publish(A, *Qu);
+  if (Qu) queue_publish(*Qu);
   __syncthreads();
   if (wave == 0) {
 #pragma unroll
@@ -909,19 +969,52 @@ MOE_INLINE void pick_refill(const Geo& cur, const Geo& nxt, bool cont, int v, in
   k = use_cur ? w : (use_nxt ? w - m : (v < cur.n ? v : 0));
 }
 
-// Products of one 32-column word for the ng (<= 4) tokens of the ring slot.
+// Table lookups of one 32-column word of ring slot s.
 template <int Q, int JW>
-MOE_INLINE void ring_word(const Ring<Q>& R, int s, int ng, uint32_t lane4,
-                          float (&acc)[kMaxTokGroup][4]) {
+MOE_INLINE void ring_decode(const Ring<Q>& R, int s, uint32_t lane4, uint32_t (&wv)[16]) {
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = word_of(R.buf[s][p], JW);
-  uint32_t wv[16];
   decode_word<Q>(w, lane4, wv);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Products of one decoded 32-column word for the ng (<= 4) tokens of ring slot s.
+template <int Q, int JW>
+MOE_INLINE void ring_dots(const Ring<Q>& R, int s, int ng, const uint32_t (&wv)[16],
+                          float (&acc)[kMaxTokGroup][4]) {
 #pragma unroll
   for (int t = 0; t < kMaxTokGroup; ++t)
     if (t < ng) dot16_bcast<JW>(acc[t], wv, R.xbuf[s][t]);
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// The four words of ring slot s.  For q <= 4 the lookups of word j + 1 are issued before the
+// products of word j, so the LDS latency is exposed once per chunk instead of once per word
+// (q >= 5 merges each looked-up pair with VALU work of its own and keeps the plain order).
+template <int Q>
+MOE_INLINE void ring_chunk(const Ring<Q>& R, int s, int ng, uint32_t lane4,
+                           float (&acc)[kMaxTokGroup][4]) {
+  uint32_t wa[16], wb[16];
+  if constexpr (Q <= 4) {
+    ring_decode<Q, 0>(R, s, lane4, wa);
+    ring_decode<Q, 1>(R, s, lane4, wb);
+    ring_dots<Q, 0>(R, s, ng, wa, acc);
+    ring_decode<Q, 2>(R, s, lane4, wa);
+    ring_dots<Q, 1>(R, s, ng, wb, acc);
+    ring_decode<Q, 3>(R, s, lane4, wb);
+    ring_dots<Q, 2>(R, s, ng, wa, acc);
+    ring_dots<Q, 3>(R, s, ng, wb, acc);
+  } else {
+    ring_decode<Q, 0>(R, s, lane4, wa);
+    ring_dots<Q, 0>(R, s, ng, wa, acc);
+    ring_decode<Q, 1>(R, s, lane4, wa);
+    ring_dots<Q, 1>(R, s, ng, wa, acc);
+    ring_decode<Q, 2>(R, s, lane4, wa);
+    ring_dots<Q, 2>(R, s, ng, wa, acc);
+    ring_decode<Q, 3>(R, s, lane4, wa);
+    ring_dots<Q, 3>(R, s, ng, wa, acc);
+  }
 }
 
 template <int MODE>
@@ -956,10 +1049,22 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
   while (true) {
     Item next;
     const int j = Qu.nxt;
-    const bool next_ok = j < total && decode_item<MODE>(A, j, sh_tiles, tiles, next);
-    const bool cont = next_ok && next.q == Q && streamable<MODE>(A, next);
+    const bool in_range = j < total;
+    bool next_ok, cont;
+    if constexpr (MODE == kPlain) {
+      next_ok = in_range && decode_item<MODE>(A, j, sh_tiles, tiles, next);
+      write_table<Q>(L, lane, wave);
+    } else {
+      // the next record's scalar loads are issued before the table is written and used after
+      // (an index past the end locates item 0, whose record always exists)
+      const ItemLoc loc = locate_item<MODE>(A, in_range ? j : 0, sh_tiles, tiles, next);
+      const RecFields f = load_record<MODE>(A, loc.slot);
+      write_table<Q>(L, lane, wave);
+      next.expert = -1;
+      next_ok = in_range && fill_item<MODE>(A, f, loc, next);
+    }
+    cont = next_ok && next.q == Q && streamable<MODE>(A, next);
     if (cont) make_geo<MODE>(A, next, nxt);
-    write_table<Q>(L, lane, wave);
     __syncthreads();
     if (cont) prefetch_lut_q<Q>(next, lane, wave, L);
     float acc[kMaxTokGroup][4] = {};
@@ -970,12 +1075,7 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
 #pragma unroll
       for (int s = 0; s < D; ++s) {
         const int v = v0 + s;
-        if (v < cur.n) {
-          ring_word<Q, 0>(R, s, cur.ng, lane4, acc);
-          ring_word<Q, 1>(R, s, cur.ng, lane4, acc);
-          ring_word<Q, 2>(R, s, cur.ng, lane4, acc);
-          ring_word<Q, 3>(R, s, cur.ng, lane4, acc);
-        }
+        if (v < cur.n) ring_chunk<Q>(R, s, cur.ng, lane4, acc);
         Geo g;
         int k;
         pick_refill(cur, nxt, cont, v, v + D, m, g, k);
@@ -986,7 +1086,7 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
 #pragma unroll
     for (int t = 0; t < kMaxTokGroup; ++t) tot[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
     reduce_and_store<MODE, kMaxTokGroup>(A, it, 0, it.n, tot, Qu);
-    i = queue_advance(A, Qu);
+    i = queue_advance(Qu);
     it = next;
     ok = next_ok;
     if (!cont) return;
@@ -1010,17 +1110,17 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
   const int srt = MODE == kDown ? A.segs : 1;
   const int total = sh_tiles * ssh + n_routed * tiles * srt;
   Queue Qu;
-  queue_init(Qu);
-  queue_request(A, Qu);
+  queue_init(A, Qu);
+  queue_request(Qu);
   int i = static_cast<int>(blockIdx.x);
   Item it;
   bool ok = i < total && decode_item<MODE>(A, i, sh_tiles, tiles, it);
   while (i < total) {
     if (!ok) {  // skip an item whose page-table descriptor is invalid
       report_invalid(A, it, MODE);
-      queue_publish(A, Qu);
+      queue_publish(Qu);
       __syncthreads();
-      i = queue_advance(A, Qu);
+      i = queue_advance(Qu);
       ok = i < total && decode_item<MODE>(A, i, sh_tiles, tiles, it);
       continue;
     }
@@ -1046,7 +1146,7 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
         case 7: run_item<MODE, 7>(A, it, Qu); break;
         default: run_item<MODE, 8>(A, it, Qu); break;
       }
-      i = queue_advance(A, Qu);
+      i = queue_advance(Qu);
       ok = i < total && decode_item<MODE>(A, i, sh_tiles, tiles, it);
     }
   }

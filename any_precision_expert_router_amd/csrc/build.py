@@ -77,6 +77,9 @@ def _check_isa(tmp: str) -> None:
         spills = isa_check.scratch_users(path)
         if spills:
             raise RuntimeError(f"register spills (scratch memory) in {os.path.basename(path)}: {spills}")
+        flat = isa_check.flat_accesses(path)
+        if flat:
+            raise RuntimeError(f"flat memory instructions in {os.path.basename(path)}: {flat[:5]}")
         m0 = isa_check.m0_foreign_uses(path)
         if m0:
             raise RuntimeError(f"M0 is used by compiler-generated code in {os.path.basename(path)}: {m0[:5]}")

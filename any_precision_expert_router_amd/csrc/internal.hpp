@@ -47,15 +47,24 @@ struct alignas(128) ExpertRecord {
   int32_t expert;             // routed expert id, -1 for the shared expert
   int32_t src_base;           // sorted position of its first pair (0 for the shared expert)
   int32_t n;                  // tokens routed to it (T for the shared expert)
-  uint8_t q[2];               // committed widths
-  uint8_t ok;                 // both page-table descriptors valid and GPU-resident
-  uint8_t reserved;
+  uint32_t meta;              // committed widths and validity, see record_meta (one dword, so
+                              // that a reader fetches it with a scalar load)
   int32_t tok[kRecTok];       // token rows of its first pairs (activation rows of gate_up)
   int32_t pair[kRecTok];      // their pair ids t*k + j (partial-sum rows of down)
   float gate[kRecTok];        // their gate weights
   int32_t pad[4];
 };
 static_assert(sizeof(ExpertRecord) == 128, "record layout");
+// meta: bits 0-7 = q of gate_up, bits 8-15 = q of down, bit 16 = both page-table descriptors
+// valid and GPU-resident.
+__host__ __device__ constexpr uint32_t record_meta(int q_gate_up, int q_down, bool ok) {
+  return static_cast<uint32_t>(q_gate_up & 0xff) | (static_cast<uint32_t>(q_down & 0xff) << 8) |
+         (ok ? 1u << 16 : 0u);
+}
+__host__ __device__ constexpr int record_q(uint32_t meta, int module) {
+  return static_cast<int>((meta >> (8 * module)) & 0xffu);
+}
+__host__ __device__ constexpr bool record_ok(uint32_t meta) { return ((meta >> 16) & 1u) != 0; }
 
 // Work counters of the FFN launches (dynamic item fetch), zeroed by the step that writes the
 // records: per launch, kQueues interleaved sub-queues, each counter on its own 128-byte line.

@@ -13,6 +13,10 @@ and branches into its block) and reports each gap that is too short.
 
 `scratch_users` reports kernels that use scratch memory (register spills).
 
+`flat_accesses` reports flat (generic address) memory instructions.  A flat load may go to LDS or
+to global memory, so its result needs a wait for every vector load in flight (vmcnt(0)), which
+drains the streaming ring; every access in these kernels must name its address space.
+
 `m0_foreign_uses` reports instructions other than "s_mov_b32 m0, ..." that name M0: the
 hand-written buffer-to-LDS loads set M0 without telling the compiler, which is only safe while
 nothing else in the kernel reads it.
@@ -172,6 +176,10 @@ def scratch_users(path: str):
             if m and name and int(m.group(1)) > 0:
                 out.append(f"{name} ({m.group(1)} bytes)")
     return out
+
+
+def flat_accesses(path: str):
+    return [t for kind, t in _program(path) if kind == "inst" and t.startswith("flat_")]
 
 
 def m0_foreign_uses(path: str):

@@ -218,10 +218,7 @@ __device__ __forceinline__ void fill_record(ExpertRecord& rec, const moe_apq_blo
   rec.planes[1] = dn.planes;
   rec.lut[0] = gu.lut;
   rec.lut[1] = dn.lut;
-  rec.q[0] = gu.q;
-  rec.q[1] = dn.q;
-  rec.ok = block_valid(gu, 2 * inter, r.H) && block_valid(dn, r.H, inter) ? 1 : 0;
-  rec.reserved = 0;
+  rec.meta = record_meta(gu.q, dn.q, block_valid(gu, 2 * inter, r.H) && block_valid(dn, r.H, inter));
 }
 
 // Records of the shared expert and of every active routed expert, and zeroed work counters.
@@ -252,7 +249,7 @@ __device__ void records_body(const GroupSmem& sm, const int32_t* pairs, const fl
     if (r.shared) {
       fill_record(rec, r.shared[0], r.shared[1], r.I_shared, r);
     } else {
-      rec.ok = 0;
+      rec.meta = record_meta(0, 0, false);
     }
     rec.expert = -1;
     rec.src_base = 0;

@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed runs of --steps calls each (eager and graph); the median is reported")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB: the known-size "
                          "dispatch that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -211,19 +213,26 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    ev_ms = ev0.elapsed_time(ev1)
+    # `repeats` timed runs of exactly `steps` calls each; the headline is the median run
+    walls, evs = [], []
+    for _ in range(args.repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        walls.append((time.perf_counter() - t0) * 1e3)
+        evs.append(ev0.elapsed_time(ev1))
+    wall_ms = float(np.median(walls))
+    ev_ms = float(np.median(evs))
     ms_per_step = wall_ms / args.steps
-    log(f"[bench] {args.steps} steps: wall {wall_ms:.2f} ms, events {ev_ms:.2f} ms "
-        f"-> {1e3 * ms_per_step:.2f} us/layer (events {1e3 * ev_ms / args.steps:.2f})")
+    log(f"[bench] {args.repeats} x {args.steps} steps: median wall {wall_ms:.2f} ms, events {ev_ms:.2f} ms "
+        f"-> {1e3 * ms_per_step:.2f} us/layer (events {1e3 * ev_ms / args.steps:.2f}); "
+        f"runs {['%.2f' % (1e3 * w / args.steps) for w in walls]} us/layer")
 
     # the same steps replayed from HIP graphs (one captured call per weight copy); every replay
     # must reproduce the eager output bit for bit
@@ -244,14 +253,17 @@ def main():
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
-        g1.record()
-        torch.cuda.synchronize()
-        graph_us = 1e3 * g0.elapsed_time(g1) / args.steps
+        gus = []
+        for _ in range(args.repeats):
+            g0 = torch.cuda.Event(enable_timing=True)
+            g1 = torch.cuda.Event(enable_timing=True)
+            g0.record()
+            for i in range(args.steps):
+                graphs[i % len(graphs)].replay()
+            g1.record()
+            torch.cuda.synchronize()
+            gus.append(1e3 * g0.elapsed_time(g1) / args.steps)
+        graph_us = float(np.median(gus))
         same = bool(torch.equal(y, y_eager))
         log(f"[bench] graph replay: {graph_us:.2f} us/layer, output identical to eager: {same}")
         assert same, "graph replay output differs from the eager call"
@@ -310,6 +322,9 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_layer": round(1e3 * ms_per_step, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "planes_only_GBs": round(planes_b / (ms_per_step * 1e-3) / 1e9, 1),
+        "repeats": args.repeats,
+        "runs_us_per_layer": [round(1e3 * w / args.steps, 2) for w in walls],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": shape.name, "tokens": T, "hidden": shape.H, "experts": shape.E,
@@ -321,8 +336,9 @@ def main():
         "per_kernel_us": {k: round(v["avg_us"], 3) for k, v in per_kernel.items()},
         "hbm_read_ceiling_GBs": round(read_ceiling, 1),
         "pct_read_ceiling": round(100 * value / read_ceiling, 2),
-        "timing": "eager moe_layer_forward calls (headline); graph_replay below replays the same call "
-                  "from captured HIP graphs",
+        "timing": f"median of {args.repeats} runs of {args.steps} eager moe_layer_forward calls "
+                  "(headline); graph_replay below replays the same calls from captured HIP graphs "
+                  "(median of as many runs)",
         "graph_replay": graph,
         "roofline": roofline,
     }
