@@ -107,8 +107,9 @@ Workspace carve_workspace(void* base, int T, int E, int H, int I, int k, int I_s
   const size_t o_part = take(w.segs * TK * H * sizeof(float));
   const size_t o_part_sh =
       take(I_shared > 0 ? w.segs_shared * static_cast<size_t>(T) * H * sizeof(float) : 0);
-  const size_t o_recs = take((static_cast<size_t>(E) + 1) * sizeof(ExpertRecord));
+  const size_t o_recs = take(max_records(T, E, k) * sizeof(ExpertRecord));
   const size_t o_ctr = take(kNumCounters * sizeof(uint32_t));
+  const size_t o_nrecs = take(sizeof(int32_t));
   w.bytes = off;
   if (base) {
     char* b = static_cast<char*>(base);
@@ -125,6 +126,7 @@ Workspace carve_workspace(void* base, int T, int E, int H, int I, int k, int I_s
     w.part_shared = reinterpret_cast<float*>(b + o_part_sh);
     w.recs = reinterpret_cast<ExpertRecord*>(b + o_recs);
     w.counters = reinterpret_cast<uint32_t*>(b + o_ctr);
+    w.n_recs = reinterpret_cast<int32_t*>(b + o_nrecs);
   }
   return w;
 }
@@ -217,7 +219,8 @@ int moe_apq_ffn(const moe_apq_block* table, int E, int H, int I, const uint16_t*
     return set_error(MOE_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                      ws.bytes);
   hipStream_t s = as_stream(stream);
-  const RecordArgs ra{table, shared, topk_gates, E, H, I, ish, T, k, ws.recs, ws.counters};
+  const RecordArgs ra{table, shared, topk_gates, E, H, I, ish, T, k, ws.recs, ws.counters, ws.n_recs,
+                      effective_dense_threshold(prefill_threshold)};
   if (int rc = launch_records(expert_offsets, sorted_pairs, active_experts, n_active, ra, s)) return rc;
   FfnArgs a{table, shared, E, H, I, k, T, ish, x, expert_offsets, sorted_pairs, active_experts,
             n_active, topk_gates, shared_scale, y, ws, prefill_threshold};
@@ -239,7 +242,8 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int T, int E, int 
     return set_error(MOE_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                      ws.bytes);
   hipStream_t s = as_stream(stream);
-  const RecordArgs ra{table, shared, ws.gates, E, H, I, ish, T, k, ws.recs, ws.counters};
+  const RecordArgs ra{table, shared, ws.gates, E, H, I, ish, T, k, ws.recs, ws.counters, ws.n_recs,
+                      effective_dense_threshold(prefill_threshold)};
   if (T <= kFusedRouteMaxT && static_cast<long>(T) * k <= kFusedRouteMaxPairs) {
     if (int rc = launch_route_group_records(logits, ws.ids, ws.gates, ws.offsets, ws.pairs, ws.active,
                                             ws.n_active, ra, s))

@@ -49,6 +49,7 @@ MOE_INLINE const AS_CONST T* cview(const void* p) { return (const AS_CONST T*)p;
 constexpr int kThreads = 64 * kWavesPerTile;
 constexpr int kMaxTokGroup = 4;                  // tokens sharing one VALU pass over the weights
 constexpr int kDenseGroup = 16;                  // tokens per MFMA pass (32x32 tile: 2 row halves x 16)
+static_assert(kDenseGroup == kRecGroupTok, "a split record holds one matrix-core token group");
 
 // LDS map of a tile workgroup (bytes):
 //   [0, 64K)        lookup tables, 4-byte slots [entry][64 lanes] unless noted.  Streaming (VALU)
@@ -175,7 +176,8 @@ struct KArgs {
   int32_t* err;
   int dense_threshold;          // tiles with at least this many tokens take the MFMA path
   int segs, segs_shared;        // column segments per down row tile (routed, shared expert)
-  const ExpertRecord* recs;     // [1 + E]: shared expert, then the active routed experts
+  const ExpertRecord* recs;     // shared expert, then the routed records (see internal.hpp)
+  const int32_t* n_recs;        // [1] routed records
   uint32_t* counter;            // work counter of this launch (null: static round-robin)
 };
 
@@ -947,8 +949,10 @@ struct Ring {
   // wait counts stay exact.
   MOE_INLINE void issue(int slot, const Geo& g, int k) {
     const size_t c = static_cast<size_t>(g.cb + k);
+    // planes stream through once: non-temporal loads keep them from displacing the cached
+    // activations and tables (measured 1-2 % faster than ordinary loads)
 #pragma unroll
-    for (int p = 0; p < Q; ++p) buf[slot][p] = g.pbase[p * g.plane_u4 + c * 64];
+    for (int p = 0; p < Q; ++p) buf[slot][p] = __builtin_nontemporal_load(&g.pbase[p * g.plane_u4 + c * 64]);
 #pragma unroll
     for (int t = 0; t < kMaxTokGroup; ++t) xbuf[slot][t] = g.xbase[t][c * 16];
   }
@@ -1104,7 +1108,7 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
   } else {
     if (A.shared) sh_tiles = (MODE == kGateUp ? A.I_shared : A.H) / kTileRows;
     tiles = (MODE == kGateUp ? A.I : A.H) / kTileRows;
-    n_routed = uniform(cview<int32_t>(A.n_active)[0]);
+    n_routed = uniform(cview<int32_t>(A.n_recs)[0]);
   }
   const int ssh = MODE == kDown ? A.segs_shared : 1;
   const int srt = MODE == kDown ? A.segs : 1;

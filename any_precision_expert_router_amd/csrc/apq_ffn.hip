@@ -24,16 +24,18 @@ int launch_apq_ffn(const FfnArgs& a, hipStream_t stream) {
   k.act = a.ws.act; k.act_shared = a.ws.act_shared;
   k.part = a.ws.part; k.part_shared = a.ws.part_shared;
   k.err = a.ws.err;
-  k.dense_threshold = a.dense_threshold > 0 ? a.dense_threshold : kDefaultDenseThreshold;
+  k.dense_threshold = effective_dense_threshold(a.dense_threshold);
+  k.n_recs = a.ws.n_recs;
   k.recs = a.ws.recs;
   const int sh = a.shared ? 1 : 0;
-  const int gu_items = sh * (a.I_shared / kGateUpTileRows) + a.E * (a.I / kGateUpTileRows);
+  const int routed = static_cast<int>(max_records(a.T, a.E, a.k)) - 2;  // routed records at most
+  const int gu_items = sh * (a.I_shared / kGateUpTileRows) + routed * (a.I / kGateUpTileRows);
   k.counter = a.ws.counters + kCtrGateUp;
   if (int rc = apq::launch_gate_up(k, gu_items, stream)) return rc;
   k.counter = a.ws.counters + kCtrDown;
   k.segs = a.ws.segs;
   k.segs_shared = sh ? a.ws.segs_shared : 1;
-  const int dn_items = (sh * k.segs_shared + a.E * k.segs) * (a.H / kRowPanel);
+  const int dn_items = (sh * k.segs_shared + routed * k.segs) * (a.H / kRowPanel);
   if (int rc = apq::launch_down(k, dn_items, stream)) return rc;
   return apq::launch_combine(a.ws.part, sh ? a.ws.part_shared : nullptr, a.T, a.H, a.k, k.segs,
                              k.segs_shared, a.y, stream);
@@ -47,7 +49,7 @@ int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y
   k.x = x;
   k.y_plain = y;
   k.segs = k.segs_shared = 1;
-  k.dense_threshold = dense_threshold > 0 ? dense_threshold : kDefaultDenseThreshold;
+  k.dense_threshold = effective_dense_threshold(dense_threshold);
   return apq::launch_plain(k, blk.rows / kRowPanel, stream);
 }
 

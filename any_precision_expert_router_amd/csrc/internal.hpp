@@ -41,6 +41,16 @@ constexpr int kWavesPerTile = 4;     // wavefronts sharing one row tile (split o
 // dependent loads (active list -> offsets -> page table -> pairs -> gates).  Record 0 is the
 // shared expert, record 1 + a the a-th active routed expert.
 constexpr int kRecTok = 4;   // tokens described in full (the streaming path's group)
+// Records and their order.  In a call with at most kRecSplitMaxPairs pairs, an expert with more
+// than kRecGroupTok tokens gets one record per group of kRecGroupTok tokens (one matrix-core
+// pass each), so that a hot expert's rows are spread over many workgroups instead of one
+// workgroup looping over its token groups.  Records of multi-token experts come first (their
+// items are the longest), then the streaming ones, each class in active-list order.
+constexpr int kRecGroupTok = 16;
+constexpr int kRecSplitMaxPairs = 1024;
+inline size_t max_records(int T, int E, int k) {
+  return static_cast<size_t>(E) + 2 + (static_cast<size_t>(T) * k + kRecGroupTok - 1) / kRecGroupTok;
+}
 struct alignas(128) ExpertRecord {
   const uint32_t* planes[2];  // gate_up, down
   const uint16_t* lut[2];
@@ -87,7 +97,8 @@ struct Workspace {
   float* part;           // fp32 [segs][T*k][H]  gate-scaled expert outputs, pair order
   float* part_shared;    // fp32 [segs_sh][T][H] scaled shared-expert outputs
   int segs, segs_shared; // down column segments (down_segments)
-  ExpertRecord* recs;    // [E + 1]
+  ExpertRecord* recs;    // [max_records(T, E, k)]
+  int32_t* n_recs;       // [1] routed records of the call
   uint32_t* counters;    // [kNumCounters]
   size_t bytes;          // total bytes the layout needs
 };
@@ -119,6 +130,8 @@ struct RecordArgs {
   int E, H, I, I_shared, T, k;
   ExpertRecord* recs;
   uint32_t* counters;
+  int32_t* n_recs;             // out: routed records written (records 1 .. n_recs)
+  int dense_threshold;         // the FFN's effective threshold (orders the records)
 };
 // Routing, grouping and the records in one single-workgroup launch (small batches).
 constexpr int kFusedRouteMaxT = 16;   // one token per wavefront of the fused workgroup
@@ -154,6 +167,9 @@ int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y
 
 // Tiles with at least this many tokens use the matrix-core (MFMA) path by default.
 constexpr int kDefaultDenseThreshold = 5;
+inline int effective_dense_threshold(int prefill_threshold) {
+  return prefill_threshold > 0 ? prefill_threshold : kDefaultDenseThreshold;
+}
 int launch_decode_indices(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
 int launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

@@ -221,30 +221,65 @@ __device__ __forceinline__ void fill_record(ExpertRecord& rec, const moe_apq_blo
   rec.meta = record_meta(gu.q, dn.q, block_valid(gu, 2 * inter, r.H) && block_valid(dn, r.H, inter));
 }
 
-// Records of the shared expert and of every active routed expert, and zeroed work counters.
-// The grouping comes from this workgroup's LDS copies (after a barrier); pairs and gates from
-// LDS when the routing ran in this workgroup, else from global memory.
-__device__ void records_body(const GroupSmem& sm, const int32_t* pairs, const float* gates,
+// Records of the shared expert and of the routed experts, the count of routed records, and
+// zeroed work counters.  One thread per active expert (blockDim >= E).  Multi-token experts'
+// records come first, split into token groups in small calls, then the streaming experts'
+// (split and order: see kRecGroupTok in internal.hpp).  The grouping comes from this workgroup's
+// LDS copies (after a barrier); pairs and gates from LDS when the routing ran in this workgroup,
+// else from global memory.
+__device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* gates,
                              const RecordArgs& r) {
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int n_act = sm.n_active;
-  for (int a = tid; a < n_act; a += blockDim.x) {
-    const int e = sm.active[a];
+  const bool split = static_cast<long>(r.T) * r.k <= kRecSplitMaxPairs;
+  int e = -1, base = 0, n = 0, groups = 0;
+  bool streaming = false;
+  if (tid < n_act) {
+    e = sm.active[tid];
+    base = sm.offsets[e];
+    n = sm.offsets[e + 1] - base;
+    streaming = n <= kRecTok && n < r.dense_threshold;
+    groups = !streaming && split && n > kRecGroupTok ? (n + kRecGroupTok - 1) / kRecGroupTok : 1;
+  }
+  // exclusive scans of (records of multi-token experts) and (streaming experts)
+  const int a0 = tid < n_act && !streaming ? groups : 0, b0 = tid < n_act && streaming ? 1 : 0;
+  int a = a0, b = b0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a2 = __shfl_up(a, off, 64), b2 = __shfl_up(b, off, 64);
+    if (lane >= off) { a += a2; b += b2; }
+  }
+  __syncthreads();  // the grouping's last reads of wave_tot are done
+  if (lane == 63) { sm.wave_tot[0][wave] = a; sm.wave_tot[1][wave] = b; }
+  __syncthreads();
+  int base_a = 0, base_b = 0, tot_a = 0, tot_b = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x) / 64; ++w) {
+    const int ta = sm.wave_tot[0][w], tb = sm.wave_tot[1][w];
+    if (w < wave) { base_a += ta; base_b += tb; }
+    tot_a += ta;
+    tot_b += tb;
+  }
+  if (tid < n_act) {
+    const int pos = streaming ? tot_a + base_b + b - b0 : base_a + a - a0;
     ExpertRecord rec;
     fill_record(rec, r.table[2 * e], r.table[2 * e + 1], r.I, r);
     rec.expert = e;
-    rec.src_base = sm.offsets[e];
-    rec.n = sm.offsets[e + 1] - rec.src_base;
+    for (int g = 0; g < groups; ++g) {
+      rec.src_base = base + g * kRecGroupTok;
+      rec.n = groups > 1 ? min(kRecGroupTok, n - g * kRecGroupTok) : n;
 #pragma unroll
-    for (int t = 0; t < kRecTok; ++t) {
-      const int p = t < rec.n ? pairs[rec.src_base + t] : 0;
-      rec.pair[t] = p;
-      rec.tok[t] = p / r.k;
-      rec.gate[t] = t < rec.n ? gates[p] : 0.0f;
+      for (int t = 0; t < kRecTok; ++t) {
+        const int p = t < rec.n ? pairs[rec.src_base + t] : 0;
+        rec.pair[t] = p;
+        rec.tok[t] = p / r.k;
+        rec.gate[t] = t < rec.n ? gates[p] : 0.0f;
+      }
+      r.recs[1 + pos + g] = rec;
     }
-    r.recs[1 + a] = rec;
   }
   if (tid == 0) {
+    r.n_recs[0] = tot_a + tot_b;
     ExpertRecord rec{};
     if (r.shared) {
       fill_record(rec, r.shared[0], r.shared[1], r.I_shared, r);
@@ -363,7 +398,8 @@ int launch_group_records(const int32_t* ids, int32_t* offsets, int32_t* pairs, i
 int launch_records(const int32_t* offsets, const int32_t* pairs, const int32_t* active,
                    const int32_t* n_active, const RecordArgs& r, hipStream_t stream) {
   ProfileScope prof("expert_records", stream);
-  hipLaunchKernelGGL(records_kernel, dim3(1), dim3(256), 0, stream, offsets, pairs, active, n_active, r);
+  hipLaunchKernelGGL(records_kernel, dim3(1), dim3(kGroupThreads), 0, stream, offsets, pairs, active,
+                     n_active, r);
   return check_launch("expert_records");
 }
 

@@ -250,10 +250,14 @@ def test_layer_k1_and_k_equals_E():
     _check_layer(wl.TINY.replace(k=8, T=6, name="k=E"))
 
 
+@pytest.mark.parametrize("T", [70, 600], ids=["split-records", "whole-records"])
 @pytest.mark.parametrize("threshold", [0, 1000], ids=["auto", "valu-max"])
-def test_layer_many_tokens_on_one_expert(threshold):
-    """More tokens per expert than one MFMA pass takes (several 16-token passes)."""
-    shape = wl.TINY.replace(E=4, k=2, T=70, name="hot experts")
+def test_layer_many_tokens_on_one_expert(threshold, T):
+    """More tokens per expert than one MFMA pass takes.  70 tokens x top-2 (140 pairs): each hot
+    expert's record is split into 16-token groups (the last one short enough for the VALU path
+    when it has at most 4 tokens); 600 tokens (1200 pairs, above the split limit): one record per
+    expert whose items loop over the 16-token groups."""
+    shape = wl.TINY.replace(E=4, k=2, T=T, name="hot experts")
     _check_layer(shape, threshold=threshold)
 
 
