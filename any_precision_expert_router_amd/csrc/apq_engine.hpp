@@ -369,6 +369,12 @@ MOE_INLINE void dot16_bcast(float (&a)[4], const uint32_t (&w)[16], const u32x4&
         "i"(4 * JW), "i"(4 * JW + 1), "i"(4 * JW + 2), "i"(4 * JW + 3));
 }
 
+// SiLU(g) * u in fp32 with the hardware exponential and reciprocal (about 1 ulp each); the result
+// is rounded to fp16, whose half-ulp (2^-11) is far larger.
+MOE_INLINE float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // Reduce the four wavefronts' partial sums (fixed order: wave 0 + 1 + 2 + 3) and apply the
 // epilogue of the mode for the ng real tokens of the group starting at g0.
 template <int MODE, int NT>
@@ -395,7 +401,7 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
       if constexpr (MODE == kGateUp) {
         const float up = __shfl_down(h, 32, 64);
         if (t < ng && lane < 32) {
-          const float a = h / (1.0f + expf(-h)) * up;  // SiLU(gate) * up
+          const float a = silu_mul(h, up);
           const int Iw = it.shared ? A.I_shared : A.I;
           uint16_t* dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + t) * Iw
                                     : A.act + static_cast<size_t>(it.src_base + g0 + t) * Iw;
@@ -653,11 +659,21 @@ MOE_INLINE void decode_word_dense(const uint32_t (&w)[Q], uint32_t lane4, uint32
 // makes sure the LDS reads of the slot's previous chunk have returned before it is refilled.
 // M0 is set here without the compiler's knowledge; the build checks that no compiler-generated
 // instruction of these kernels reads M0.
-MOE_INLINE void lds_dma16(uint32_t lds_addr, uint32_t voff, __amdgpu_buffer_rsrc_t rsrc, uint32_t soff) {
+MOE_INLINE void lds_dma16(uint32_t lds_addr, uint32_t voff, const u32x4& rsrc, uint32_t soff) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory");
+}
+
+// Buffer resource of `bytes` bytes at `base` (raw buffer, no stride), as four wave-uniform
+// dwords, each read from the first lane, so that the asm's scalar operand is always in SGPRs
+// whatever the register pressure around it.
+MOE_INLINE u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(uniform(static_cast<int>(a & 0xffffffffu))),
+               static_cast<uint32_t>(uniform(static_cast<int>((a >> 32) & 0xffffu))),
+               static_cast<uint32_t>(uniform(static_cast<int>(bytes))), 0x00020000u};
 }
 
 template <int Q>
@@ -668,7 +684,7 @@ struct DenseStream {
   const AS_GLOBAL u32x4* pbase;
   size_t plane_u4;
   int cb, ce;
-  __amdgpu_buffer_rsrc_t xrsrc;
+  u32x4 xrsrc;  // buffer resource of the activation rows (scalar registers)
   uint32_t rowoff[kDma];            // per lane: DMA i's byte offset (token lane%16, piece 4i + lane/16)
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, piece 0
@@ -767,8 +783,7 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
     base = A.x;
     rows_total = A.T;
   }
-  S.xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), static_cast<short>(0),
-                                              static_cast<int>(rows_total * C * 2), 0x00020000);
+  S.xrsrc = buffer_rsrc(base, static_cast<uint32_t>(rows_total * C * 2));
   // token lane % 16 (tokens past ng re-read token g0's row; their columns are dropped)
   const int t = lane & 15;
   const int tt = g0 + (t < ng ? t : 0);
@@ -849,7 +864,7 @@ MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, i
         // gate row r0 + m and up row row_hi + m meet in the same lane and register
         if (live) {
           const float g = lo[i];
-          act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(g / (1.0f + expf(-g)) * hi[i]));
+          act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(silu_mul(g, hi[i])));
         }
       } else {
         if (live) {

@@ -37,6 +37,9 @@ def hipcc() -> str:
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
     out = os.path.join(PKG, LIB_NAME)
+    # a failed build must not leave the previous library behind for tests to load
+    if os.path.exists(out):
+        os.remove(out)
     with tempfile.TemporaryDirectory(prefix="moe_apq_build_") as tmp:
         objs, procs = [], []
         for src in SOURCES:
