@@ -26,6 +26,9 @@ It is the plain, slow definition of what the layer computes, in float64 NumPy:
 5. ``layer_forward`` the gate-weighted combine y_t = sum_j g_tj o_tj, plus an optional
                     always-on shared expert (PagedWeight, Key Components 3: one fused kernel
                     reads the planes and LUTs of blocks of different widths).
+6. ``routing_stats`` per-expert selection count and routing mass of a call, and the gate mass
+                    on non-resident experts (PagedWeight, Key Components 2; "Which Expert
+                    Misses Are Worth Waiting For?", Methodology: substituted gate mass).
 
 Readings where the pages are silent (all listed in the design notes of the repository):
 the parent width is 8 bits and plane p holds bit 7-p of the parent index, so the q-bit index
@@ -259,6 +262,42 @@ def layer_forward(x: np.ndarray, logits: np.ndarray, k: int, get_block: BlockGet
         y[rows] += s[rows, None] * _ffn_from_getter(shared, 0, x64[rows])
     return dict(ids=ids, gates=gates, offsets=offsets, pairs=pairs, active=active,
                 n_active=n_active, y=y)
+
+
+# --------------------------------------------------------------------------------------------
+# 6. Online routing statistics and the substituted gate mass
+# --------------------------------------------------------------------------------------------
+def routing_stats(ids: np.ndarray, gates: np.ndarray, E: int,
+                  resident: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, float, float]:
+    """Routing mass of one call and the gate mass that would be substituted.
+
+    PagedWeight, Key Components 2 (online routing statistics): an expert's routing mass is how
+    often and with what weight the router selects it -- here count[e] = number of (token, slot)
+    pairs routed to e and mass[e] = the sum of their gate weights.  "Which Expert Misses Are
+    Worth Waiting For?", Methodology: the substituted gate mass m is the normalised sum of the
+    gate weights of the substituted experts; with a resident set and every miss substituted
+    (no policy fetches any), substituted = sum of g over pairs whose expert is not resident and
+    m = substituted / total, total = sum of every g.  Sums run over the pairs p = t*k + j in
+    ascending order.  Returns (count int64 [E], mass float64 [E], substituted, total).
+    """
+    flat_ids = np.asarray(ids).reshape(-1)
+    flat_g = np.asarray(gates, dtype=np.float64).reshape(-1)
+    assert flat_ids.shape == flat_g.shape
+    res = np.ones(E, dtype=bool) if resident is None else np.asarray(resident).reshape(-1) != 0
+    count = np.zeros(E, dtype=np.int64)
+    mass = np.zeros(E, dtype=np.float64)
+    substituted = 0.0
+    total = 0.0
+    for p in range(flat_ids.size):
+        e = int(flat_ids[p])
+        assert 0 <= e < E
+        g = float(flat_g[p])
+        count[e] += 1
+        mass[e] += g
+        total += g
+        if not res[e]:
+            substituted += g
+    return count, mass, substituted, total
 
 
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:

@@ -375,3 +375,36 @@ def test_generators_are_deterministic_and_luts_nested():
     w = wl.gen_widths(wl.QWEN3_NEXT_80B_A3B)
     assert (w[:, 0] == 8).sum() >= 128 and set(np.unique(w).tolist()) <= {3, 4, 5, 6, 8}
     assert np.all(wl.gen_widths(wl.QWEN15_MOE_A27B) == 4)
+
+
+# ---- routing statistics --------------------------------------------------------------------
+def test_routing_stats_match_bincount_and_mass_sums_to_tokens():
+    """count = numpy.bincount of the ids, mass = bincount weighted by the gates (library
+    routines), the counts add up to T*k and, since each token's gates sum to 1, the masses add
+    up to T."""
+    r = np.random.default_rng(11)
+    T, E, k = 29, 13, 3
+    ids, gates = oracle.route_topk(r.standard_normal((T, E)), k)
+    count, mass, sub, tot = oracle.routing_stats(ids, gates, E)
+    np.testing.assert_array_equal(count, np.bincount(ids.ravel(), minlength=E))
+    np.testing.assert_allclose(mass, np.bincount(ids.ravel(), weights=gates.ravel(), minlength=E),
+                               rtol=1e-15, atol=1e-15)
+    assert count.sum() == T * k
+    assert abs(mass.sum() - T) < 1e-12 and abs(tot - T) < 1e-12
+    assert sub == 0.0   # every expert resident
+
+
+def test_substituted_mass_special_cases_and_hand_example():
+    """No expert resident: everything is substituted (m = 1); all resident: m = 0.  Hand case:
+    token 0 picks experts (2, 0) with gates (0.7, 0.3), token 1 picks (1, 2) with (0.6, 0.4);
+    with only expert 2 resident, the substituted mass is 0.3 + 0.6 of a total 2.0."""
+    ids = np.array([[2, 0], [1, 2]])
+    gates = np.array([[0.7, 0.3], [0.6, 0.4]])
+    count, mass, sub, tot = oracle.routing_stats(ids, gates, 4, resident=np.array([0, 0, 1, 0]))
+    np.testing.assert_array_equal(count, [1, 1, 2, 0])
+    np.testing.assert_allclose(mass, [0.3, 0.6, 1.1, 0.0], rtol=0, atol=1e-15)
+    assert abs(sub - 0.9) < 1e-15 and abs(tot - 2.0) < 1e-15
+    _, _, sub0, tot0 = oracle.routing_stats(ids, gates, 4, resident=np.zeros(4))
+    assert sub0 == tot0
+    _, _, sub1, _ = oracle.routing_stats(ids, gates, 4, resident=np.ones(4))
+    assert sub1 == 0.0
