@@ -30,6 +30,7 @@ EXPORTED = (
     "moe_route_topk", "moe_group_by_expert", "moe_apq_ffn", "moe_layer_forward",
     "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
     "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_hbm_read_probe",
+    "moe_routing_stats", "moe_workspace_routing",
     "moe_last_error",
 )
 
@@ -78,6 +79,8 @@ def _load():
         "moe_profile_start": ([], I),
         "moe_profile_stop": ([I, P, P, P], I),
         "moe_hbm_read_probe": ([P, Z, P, S], I),
+        "moe_routing_stats": ([P, P, P, I, I, I, P, P, P, P, S], I),
+        "moe_workspace_routing": ([P, Z, I, I, I, I, I, I, P, P, P, P], I),
         "moe_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -189,6 +192,35 @@ def moe_hbm_read_probe(buf, sink, stream=None) -> None:
     """Stream-read `buf` (device tensor, size a multiple of 1 KiB) once; XOR of the data into sink."""
     _check("moe_hbm_read_probe", _lib.moe_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
                                                          _ptr(sink), _stream(stream)))
+
+
+def moe_routing_stats(expert_offsets, sorted_pairs, topk_gates, T, k, E, count, mass, mass_sums,
+                      resident=None, stream=None) -> None:
+    """Add one call's per-expert counts (uint64 [E] as int64 tensor), gate masses (float64 [E])
+    and [non-resident mass, total mass] (float64 [2]) to the accumulators (device tensors)."""
+    _check("moe_routing_stats", _lib.moe_routing_stats(
+        _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(topk_gates), T, k, E,
+        None if resident is None else _ptr(resident), _ptr(count), _ptr(mass), _ptr(mass_sums),
+        _stream(stream)))
+
+
+def moe_workspace_routing(workspace, T, E, H, I, k, I_shared=0) -> dict:
+    """Views into `workspace` (uint8 device tensor) of the routing results a moe_layer_forward
+    call left there: ids / pairs int32 [T*k], gates float32 [T*k], offsets int32 [E+1]."""
+    import torch
+    ptrs = [ctypes.c_void_p() for _ in range(4)]
+    _check("moe_workspace_routing", _lib.moe_workspace_routing(
+        _ptr(workspace), workspace.numel(), T, E, H, I, k, I_shared,
+        *[ctypes.byref(p) for p in ptrs]))
+    base = workspace.data_ptr()
+
+    def view(p, n, dtype):
+        off = p.value - base
+        return workspace[off: off + n * 4].view(dtype)
+
+    TK = T * k
+    return {"ids": view(ptrs[0], TK, torch.int32), "gates": view(ptrs[1], TK, torch.float32),
+            "offsets": view(ptrs[2], E + 1, torch.int32), "pairs": view(ptrs[3], TK, torch.int32)}
 
 
 def moe_profile_start() -> None:

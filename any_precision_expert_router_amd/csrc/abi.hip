@@ -295,6 +295,37 @@ int moe_check_device_error(void* workspace, size_t ws_bytes, void* stream) {
                    word[1], word[2] == 0 ? "gate_up" : "down");
 }
 
+int moe_routing_stats(const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                      const float* topk_gates, int T, int k, int E, const uint8_t* resident,
+                      uint64_t* count, double* mass, double* mass_sums, void* stream) {
+  clear_error();
+  if (int rc = check_route_args(T, E, k)) return rc;
+  if (!expert_offsets || !count || !mass || !mass_sums) return set_error(MOE_EINVAL, "NULL pointer argument");
+  if (T > 0 && (!sorted_pairs || !topk_gates)) return set_error(MOE_EINVAL, "NULL pointer argument");
+  return launch_routing_stats(expert_offsets, sorted_pairs, topk_gates, E, resident,
+                              reinterpret_cast<unsigned long long*>(count), mass, mass_sums,
+                              as_stream(stream));
+}
+
+int moe_workspace_routing(void* workspace, size_t ws_bytes, int T, int E, int H, int I, int k,
+                          int I_shared, int32_t** topk_ids, float** topk_gates,
+                          int32_t** expert_offsets, int32_t** sorted_pairs) {
+  clear_error();
+  if (int rc = check_route_args(T, E, k)) return rc;
+  if (int rc = check_ffn_dims(H, I, I_shared, I_shared > 0)) return rc;
+  if (!topk_ids || !topk_gates || !expert_offsets || !sorted_pairs)
+    return set_error(MOE_EINVAL, "NULL pointer argument");
+  const Workspace ws = carve_workspace(workspace, T, E, H, I, k, I_shared);
+  if (!workspace || ws_bytes < ws.bytes)
+    return set_error(MOE_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                     ws.bytes);
+  *topk_ids = ws.ids;
+  *topk_gates = ws.gates;
+  *expert_offsets = ws.offsets;
+  *sorted_pairs = ws.pairs;
+  return MOE_OK;
+}
+
 int moe_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   clear_error();
   if (!buf || !sink) return set_error(MOE_EINVAL, "NULL pointer argument");

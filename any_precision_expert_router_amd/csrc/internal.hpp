@@ -171,6 +171,9 @@ inline int effective_dense_threshold(int prefill_threshold) {
   return prefill_threshold > 0 ? prefill_threshold : kDefaultDenseThreshold;
 }
 int launch_decode_indices(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
+int launch_routing_stats(const int32_t* offsets, const int32_t* pairs, const float* gates, int E,
+                         const uint8_t* resident, unsigned long long* count, double* mass,
+                         double* sums, hipStream_t stream);
 int launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace moeapq

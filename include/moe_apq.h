@@ -204,6 +204,43 @@ int moe_profile_stop(int max_kernels, char* names_out, double* total_ms_out,
                      int32_t* launches_out);
 
 /*
+ * Online routing statistics of one call, added to caller-owned accumulators.
+ *
+ * Source: PagedWeight, Key Components 2 (online routing statistics): an expert's routing mass is
+ * how often and with what weight it is selected.  "Which Expert Misses Are Worth Waiting For?",
+ * Methodology: the substituted gate mass m is the normalised sum of the gate weights of the
+ * substituted experts; here, with every non-resident expert substituted,
+ * m = mass_sums[0] / mass_sums[1].
+ *
+ * Inputs are one call's grouping and gates (device): expert_offsets [E+1] and sorted_pairs [T*k]
+ * as written by moe_group_by_expert (or left by moe_layer_forward, see moe_workspace_routing),
+ * topk_gates [T*k] fp32 in pair order p = t*k + j.  resident: device uint8 [E], 0 = the expert
+ * is not GPU-resident; NULL = all resident.
+ * Accumulators (device, caller-owned, never reset by the library -- zero them to start a
+ * window; no decay): count [E] uint64 += pairs routed to expert e; mass [E] double += the sum of
+ * their gates; mass_sums[0] double += gate mass of pairs whose expert is not resident,
+ * mass_sums[1] += the total gate mass (T when every token's gates sum to 1).
+ * Sums are taken in double, per expert in ascending pair order, then across experts in a fixed
+ * order: the results do not depend on timing.  Calls that share accumulators must be ordered
+ * (one stream).  Errors: MOE_EINVAL for bad T/E/k or NULL arguments.
+ */
+int moe_routing_stats(const int32_t* expert_offsets, const int32_t* sorted_pairs,
+                      const float* topk_gates, int T, int k, int E, const uint8_t* resident,
+                      uint64_t* count, double* mass, double* mass_sums, void* stream);
+
+/*
+ * Device addresses of the routing results that moe_layer_forward leaves in its workspace:
+ * topk ids [T*k] int32, gates [T*k] fp32, expert offsets [E+1] int32 and sorted pairs [T*k]
+ * int32 (same layouts as moe_route_topk / moe_group_by_expert).  They are valid after the
+ * layer call on the workspace's stream and until the workspace is used again.  Host-only: no
+ * device access.  The shape arguments are those of moe_workspace_bytes.  Errors: MOE_EINVAL,
+ * MOE_EWORKSPACE (workspace NULL or smaller than moe_workspace_bytes()).
+ */
+int moe_workspace_routing(void* workspace, size_t ws_bytes, int T, int E, int H, int I, int k,
+                          int I_shared, int32_t** topk_ids, float** topk_gates,
+                          int32_t** expert_offsets, int32_t** sorted_pairs);
+
+/*
  * Diagnostic: read `bytes` of device memory at `buf` once, with the access pattern that streams
  * fastest on this device (every wavefront reads one contiguous run in 1-KiB non-temporal loads,
  * 16 in flight), and XOR every 32-bit word of it into `*sink` (device, 4 bytes, stream-ordered

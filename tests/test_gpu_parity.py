@@ -344,3 +344,60 @@ def test_hbm_read_probe_reads_every_word_once(kib):
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
+
+
+# ------------------------------------------------------------------------------------------
+# online routing statistics and the substituted gate mass
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,k", [(37, 20, 3), (64, 512, 10), (16, 60, 4), (5, 3, 3), (300, 1024, 32)])
+def test_routing_stats_match_oracle_and_accumulate(T, E, k):
+    """Counts bit-exact; per-expert masses bit-exact against the oracle run on the same fp32
+    gates (both sum in double in ascending pair order); the two totals within 1e-12 (the GPU
+    adds the experts' sums in a tree).  Two calls double every accumulator; a quarter of the
+    experts resident."""
+    say(f"routing stats T={T} E={E} k={k}")
+    r = np.random.default_rng(T * 7 + E + k)
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    logits[:, 1] += 3.0   # a hot expert
+    ids, gates = _route_gpu(logits, k)
+    off, pairs, _, _ = _group_gpu(ids, E)
+    resident = (r.random(E) < 0.25).astype(np.uint8)
+    count = torch.zeros(E, dtype=torch.int64, device=DEV)
+    mass = torch.zeros(E, dtype=torch.float64, device=DEV)
+    sums = torch.zeros(2, dtype=torch.float64, device=DEV)
+    for _ in range(2):
+        apq.moe_routing_stats(off, pairs, gates, T, k, E, count, mass, sums, resident=_t(resident))
+    torch.cuda.synchronize()
+    g = gates.cpu().numpy().astype(np.float64)
+    c_ref, m_ref, s_ref, t_ref = oracle.routing_stats(ids.cpu().numpy(), g, E, resident=resident)
+    np.testing.assert_array_equal(count.cpu().numpy(), 2 * c_ref)
+    np.testing.assert_array_equal(mass.cpu().numpy(), 2 * m_ref)
+    s = sums.cpu().numpy()
+    assert abs(s[0] - 2 * s_ref) <= 1e-12 * max(1.0, t_ref) and abs(s[1] - 2 * t_ref) <= 1e-12 * t_ref
+    # against the oracle's own float64 routing: the fp32 gates differ by rounding only
+    _, m64, s64, t64 = oracle.routing_stats(*oracle.route_topk(logits, k), E, resident=resident)
+    np.testing.assert_allclose(mass.cpu().numpy(), 2 * m64, rtol=1e-6, atol=1e-6)
+    assert abs(s[1] - 2 * t64) <= 1e-5 * T and abs(s[0] - 2 * s64) <= 1e-5 * T
+
+
+def test_routing_stats_from_a_layer_calls_workspace():
+    """The routing results a moe_layer_forward call leaves in its workspace give the same
+    statistics as routing and grouping the same logits separately."""
+    shape = wl.QWEN3_NEXT_80B_A3B.replace(H=256, I=256, name="stats from layer")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    _, ws = _run_layer(shape, inputs, dl)
+    view = apq.moe_workspace_routing(ws, shape.T, shape.E, shape.H, shape.I, shape.k, shape.I_shared)
+    E, T, k = shape.E, shape.T, shape.k
+    acc = [torch.zeros(E, dtype=torch.int64, device=DEV), torch.zeros(E, dtype=torch.float64, device=DEV),
+           torch.zeros(2, dtype=torch.float64, device=DEV)]
+    apq.moe_routing_stats(view["offsets"], view["pairs"], view["gates"], T, k, E, *acc)
+    ids, gates = _route_gpu(inputs.logits, k)
+    off, pairs, _, _ = _group_gpu(ids, E)
+    np.testing.assert_array_equal(view["ids"].cpu().numpy().reshape(T, k), ids.cpu().numpy())
+    ref = [torch.zeros_like(a) for a in acc]
+    apq.moe_routing_stats(off, pairs, gates, T, k, E, *ref)
+    torch.cuda.synchronize()
+    for a, b in zip(acc, ref):
+        np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
+    assert acc[2][0].item() == 0.0   # no resident mask: nothing substituted

@@ -108,3 +108,28 @@ def test_workspace_bytes_cover_the_sections():
     # the shared expert's 44-chunk down rows are cut into 3 column segments, each with its own
     # fp32 partial sums [T][H]
     assert n - lib.moe_workspace_bytes(T, E, H, I, k, 0) >= T * Ish * 2 + 3 * T * H * 4
+
+
+def test_workspace_routing_addresses_lie_inside_the_workspace():
+    """moe_workspace_routing is host-only: with a made-up base address it returns the addresses
+    of the ids, gates, offsets and pairs sections, disjoint, 4-byte aligned and inside the
+    workspace; a short workspace and bad shapes are rejected."""
+    import ctypes
+    lib = apq.lib()
+    T, E, H, I, k, Ish = 16, 60, 2048, 1408, 4, 5632
+    n = lib.moe_workspace_bytes(T, E, H, I, k, Ish)
+    base = 1 << 40
+    ptrs = [ctypes.c_void_p() for _ in range(4)]
+    rc = lib.moe_workspace_routing(base, n, T, E, H, I, k, Ish, *[ctypes.byref(p) for p in ptrs])
+    assert rc == apq.MOE_OK
+    spans = sorted((p.value, p.value + size) for p, size in
+                   zip(ptrs, [4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k]))
+    for lo, hi in spans:
+        assert base <= lo < hi <= base + n and lo % 4 == 0
+    for (lo0, hi0), (lo1, hi1) in zip(spans, spans[1:]):
+        assert hi0 <= lo1
+    assert lib.moe_workspace_routing(base, n - 1, T, E, H, I, k, Ish,
+                                     *[ctypes.byref(p) for p in ptrs]) == apq.MOE_EWORKSPACE
+    assert lib.moe_workspace_routing(base, n, T, 0, H, I, k, Ish,
+                                     *[ctypes.byref(p) for p in ptrs]) == apq.MOE_EINVAL
+    assert lib.moe_routing_stats(None, None, None, T, k, E, None, None, None, None, None) == apq.MOE_EINVAL
