@@ -297,6 +297,29 @@ def main():
     per_kernel = {k: {"avg_us": 1e3 * v[0] / v[1], "launches": v[1]} for k, v in prof.items()}
     log("[bench] per-kernel (events): " + ", ".join(f"{k} {v['avg_us']:.2f} us" for k, v in per_kernel.items()))
 
+    # rows beyond the layer call, timed on the same workload: the online routing statistics of
+    # each timed call, read from the routing results the call left in its workspace
+    view = apq.moe_workspace_routing(ws, T, shape.E, shape.H, shape.I, shape.k, shape.I_shared)
+    acc = [torch.zeros(shape.E, dtype=torch.int64, device=dev),
+           torch.zeros(shape.E, dtype=torch.float64, device=dev),
+           torch.zeros(2, dtype=torch.float64, device=dev)]
+    resident = (torch.arange(shape.E, device=dev) % 4 == 0).to(torch.uint8)
+    apq.moe_profile_start()
+    for _ in range(args.steps):
+        apq.moe_routing_stats(view["offsets"], view["pairs"], view["gates"], T, shape.k, shape.E,
+                              *acc, resident=resident, stream=stream)
+    torch.cuda.synchronize()
+    sprof = apq.moe_profile_stop()
+    stats_us = 1e3 * sprof["routing_stats"][0] / sprof["routing_stats"][1]
+    m = float(acc[2][0] / acc[2][1]) if float(acc[2][1]) > 0 else 0.0
+    next_rows = {"routing_stats": {
+        "us_per_call": round(stats_us, 3),
+        "bytes_per_call": int(4 * (shape.E + 1) + 8 * T * shape.k + 33 * shape.E),
+        "substituted_gate_mass_m": round(m, 5),
+        "note": "per-expert counts + gate mass + non-resident mass (a quarter of the experts "
+                "resident), from the routing results of a layer call; latency-bound single workgroup"}}
+    log(f"[bench] routing statistics: {stats_us:.2f} us per call, m = {m:.4f}")
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18   # fp32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -340,6 +363,7 @@ def main():
                   "(headline); graph_replay below replays the same calls from captured HIP graphs "
                   "(median of as many runs)",
         "graph_replay": graph,
+        "next_rows": next_rows,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
