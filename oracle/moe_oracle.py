@@ -29,6 +29,8 @@ It is the plain, slow definition of what the layer computes, in float64 NumPy:
 6. ``routing_stats`` per-expert selection count and routing mass of a call, and the gate mass
                     on non-resident experts (PagedWeight, Key Components 2; "Which Expert
                     Misses Are Worth Waiting For?", Methodology: substituted gate mass).
+7. ``plan_widths``  the greedy width planner: lowest damage per byte saved until a memory
+                    target is met (PagedWeight, Key Components 2).
 
 Readings where the pages are silent (all listed in the design notes of the repository):
 the parent width is 8 bits and plane p holds bit 7-p of the parent index, so the q-bit index
@@ -298,6 +300,46 @@ def routing_stats(ids: np.ndarray, gates: np.ndarray, E: int,
         if not res[e]:
             substituted += g
     return count, mass, substituted, total
+
+
+# --------------------------------------------------------------------------------------------
+# 7. Width planning: greedy lowest-damage-per-byte reductions
+# --------------------------------------------------------------------------------------------
+def block_bytes(rows: int, cols: int, q: int) -> int:
+    """Resident bytes of a block at width q: q planes of rows*cols/8 bytes + an fp16 LUT of
+    2**q entries per row (PagedWeight, Key Components 1: bit-planes + LUTs)."""
+    rows, cols, q = int(rows), int(cols), int(q)
+    return rows * cols * q // 8 + rows * (1 << q) * 2
+
+
+def plan_widths(q_cur, q_floor, rows, cols, damage, mult, target_bytes: int):
+    """Greedy width plan (PagedWeight, Key Components 2: the planner scores the damage of
+    bit-width reductions and, when a memory target must be met, picks greedily the reductions
+    of lowest damage per byte saved).  Reading of the unstated details: a reduction is one step
+    q -> q-1 of one block, allowed while q-1 >= q_floor[i]; its cost is
+    mult[i] * (damage[i][q-1] - damage[i][q]) / (bytes saved by the step), damage[i][w] being
+    the block's damage score at width w (index w-1 of a row of 8); the cheapest step is taken
+    (ties: lower block index), the block's next step becomes a candidate, and steps are taken
+    until the bytes saved reach target_bytes or none is left.  Costs are compared in float64.
+    Returns (q_new, bytes_saved).
+    """
+    q = [int(v) for v in q_cur]
+    n = len(q)
+    saved = 0
+    while saved < target_bytes:
+        best, best_cost = -1, None
+        for i in range(n):
+            if q[i] - 1 < max(1, int(q_floor[i])):
+                continue
+            step = block_bytes(rows[i], cols[i], q[i]) - block_bytes(rows[i], cols[i], q[i] - 1)
+            cost = float(mult[i]) * (float(damage[i][q[i] - 2]) - float(damage[i][q[i] - 1])) / step
+            if best < 0 or cost < best_cost:
+                best, best_cost = i, cost
+        if best < 0:
+            break
+        saved += block_bytes(rows[best], cols[best], q[best]) - block_bytes(rows[best], cols[best], q[best] - 1)
+        q[best] -= 1
+    return np.array(q, dtype=np.uint8), saved
 
 
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:

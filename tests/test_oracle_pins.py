@@ -408,3 +408,72 @@ def test_substituted_mass_special_cases_and_hand_example():
     assert sub0 == tot0
     _, _, sub1, _ = oracle.routing_stats(ids, gates, 4, resident=np.ones(4))
     assert sub1 == 0.0
+
+
+# ---- width planner -------------------------------------------------------------------------
+def test_block_bytes_closed_form():
+    """q planes of R*C/8 bytes plus an fp16 LUT of 2**q entries per row."""
+    assert oracle.block_bytes(64, 128, 4) == 64 * 128 * 4 // 8 + 64 * 16 * 2
+    assert oracle.block_bytes(2816, 2048, 8) == 2816 * 2048 + 2816 * 256 * 2
+
+
+def test_planner_hand_example():
+    """Two blocks of one shape (each step saves the same bytes); block 0's step 4->3 costs 1.0,
+    block 1's 4->3 costs 0.5 and its 3->2 costs 3.0.  A target of two steps takes block 1's
+    4->3 (0.5), then block 0's 4->3 (1.0) rather than block 1's 3->2 (3.0)."""
+    R, C = 64, 128
+    step43 = oracle.block_bytes(R, C, 4) - oracle.block_bytes(R, C, 3)
+    dmg = np.zeros((2, 8))
+    dmg[0, 2] = 1.0 * step43            # damage at width 3 (index 2), width 4 has damage 0
+    dmg[1, 2] = 0.5 * step43
+    dmg[1, 1] = dmg[1, 2] + 3.0 * (oracle.block_bytes(R, C, 3) - oracle.block_bytes(R, C, 2))
+    q, saved = oracle.plan_widths([4, 4], [1, 1], [R, R], [C, C], dmg, [1.0, 1.0], 2 * step43)
+    np.testing.assert_array_equal(q, [3, 3])
+    assert saved == 2 * step43
+    # one step only: the cheaper block
+    q, _ = oracle.plan_widths([4, 4], [1, 1], [R, R], [C, C], dmg, [1.0, 1.0], 1)
+    np.testing.assert_array_equal(q, [4, 3])
+    # a damage multiplier of 3 on block 1 (a hot expert) makes block 0 the cheaper first step
+    q, _ = oracle.plan_widths([4, 4], [1, 1], [R, R], [C, C], dmg, [1.0, 3.0], 1)
+    np.testing.assert_array_equal(q, [3, 4])
+
+
+def test_planner_invariants_and_exhaustive_optimality_of_each_step():
+    """Random instances: floors are respected, the plan stops as soon as the target is met, an
+    unreachable target reduces every block to its floor, and (definition of the greedy rule)
+    replaying the plan step by step, each taken step is no more costly than any step available
+    at that moment (checked by enumerating all of them)."""
+    r = np.random.default_rng(5)
+    for _ in range(40):
+        n = int(r.integers(1, 7))
+        rows = r.choice([64, 128], n)
+        cols = r.choice([128, 256], n)
+        qc = r.integers(2, 9, n)
+        fl = np.minimum(qc, r.integers(1, 5, n))
+        dmg = np.cumsum(r.random((n, 8))[:, ::-1], axis=1)[:, ::-1]   # non-increasing in width
+        mult = r.uniform(0.5, 3.0, n)
+        full = sum(oracle.block_bytes(rows[i], cols[i], qc[i]) - oracle.block_bytes(rows[i], cols[i], fl[i])
+                   for i in range(n))
+        target = int(r.integers(0, full + 2000))
+        q, saved = oracle.plan_widths(qc, fl, rows, cols, dmg, mult, target)
+        assert np.all(q >= fl) and np.all(q <= qc)
+        assert saved == sum(oracle.block_bytes(rows[i], cols[i], qc[i]) - oracle.block_bytes(rows[i], cols[i], q[i])
+                            for i in range(n))
+        if target > full:
+            np.testing.assert_array_equal(q, fl)
+        else:
+            assert saved >= target
+        # replay: every taken step is a minimum-cost available step at its time
+        cur = [int(v) for v in qc]
+        done = 0
+        while done < saved:
+            costs = {}
+            for i in range(n):
+                if cur[i] - 1 >= max(1, fl[i]):
+                    st = oracle.block_bytes(rows[i], cols[i], cur[i]) - oracle.block_bytes(rows[i], cols[i], cur[i] - 1)
+                    costs[i] = mult[i] * (dmg[i][cur[i] - 2] - dmg[i][cur[i] - 1]) / st
+            i = min(costs, key=lambda j: (costs[j], j))
+            assert q[i] < cur[i]     # the plan took this block's step
+            done += oracle.block_bytes(rows[i], cols[i], cur[i]) - oracle.block_bytes(rows[i], cols[i], cur[i] - 1)
+            cur[i] -= 1
+        np.testing.assert_array_equal(cur, q)
