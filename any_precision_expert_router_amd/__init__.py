@@ -30,7 +30,7 @@ EXPORTED = (
     "moe_route_topk", "moe_group_by_expert", "moe_apq_ffn", "moe_layer_forward",
     "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
     "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_hbm_read_probe",
-    "moe_routing_stats", "moe_workspace_routing",
+    "moe_routing_stats", "moe_workspace_routing", "moe_commit_blocks", "moe_plan_widths",
     "moe_last_error",
 )
 
@@ -81,6 +81,8 @@ def _load():
         "moe_hbm_read_probe": ([P, Z, P, S], I),
         "moe_routing_stats": ([P, P, P, I, I, I, P, P, P, P, S], I),
         "moe_workspace_routing": ([P, Z, I, I, I, I, I, I, P, P, P, P], I),
+        "moe_commit_blocks": ([P, P, P, I, S], I),
+        "moe_plan_widths": ([I, P, P, P, P, P, P, ctypes.c_int64, P, P], I),
         "moe_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -221,6 +223,33 @@ def moe_workspace_routing(workspace, T, E, H, I, k, I_shared=0) -> dict:
     TK = T * k
     return {"ids": view(ptrs[0], TK, torch.int32), "gates": view(ptrs[1], TK, torch.float32),
             "offsets": view(ptrs[2], E + 1, torch.int32), "pairs": view(ptrs[3], TK, torch.int32)}
+
+
+def moe_commit_blocks(table, index, descs, stream=None) -> None:
+    """Overwrite page-table entries `index` (ints) of the device table (uint8 tensor of
+    32-byte entries) with `descs` (ApqBlock list), in stream order."""
+    n = len(index)
+    idx = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in index])
+    arr = (ApqBlock * max(n, 1))(*descs)
+    _check("moe_commit_blocks", _lib.moe_commit_blocks(_ptr(table), idx, arr, n, _stream(stream)))
+
+
+def moe_plan_widths(q_cur, q_floor, rows, cols, damage, mult, target_bytes):
+    """Greedy width plan on the host.  Array arguments are NumPy-convertible; damage is [n, 8]
+    (damage[i, w-1] = score at width w).  Returns (q_new uint8 [n], bytes saved)."""
+    import numpy as np
+    q_cur = np.ascontiguousarray(q_cur, dtype=np.uint8)
+    n = q_cur.size
+    args = [np.ascontiguousarray(q_floor, dtype=np.uint8), np.ascontiguousarray(rows, dtype=np.int32),
+            np.ascontiguousarray(cols, dtype=np.int32),
+            np.ascontiguousarray(np.asarray(damage, dtype=np.float32).reshape(n * 8)),
+            np.ascontiguousarray(mult, dtype=np.float32)]
+    q_new = np.zeros(n, dtype=np.uint8)
+    saved = ctypes.c_int64()
+    _check("moe_plan_widths", _lib.moe_plan_widths(
+        n, q_cur.ctypes.data, *[a.ctypes.data for a in args], int(target_bytes), q_new.ctypes.data,
+        ctypes.byref(saved)))
+    return q_new, int(saved.value)
 
 
 def moe_profile_start() -> None:

@@ -307,6 +307,22 @@ int moe_routing_stats(const int32_t* expert_offsets, const int32_t* sorted_pairs
                               as_stream(stream));
 }
 
+int moe_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
+                      void* stream) {
+  clear_error();
+  if (n < 0) return set_error(MOE_EINVAL, "n=%d < 0", n);
+  if (n == 0) return MOE_OK;
+  if (!table || !index || !desc) return set_error(MOE_EINVAL, "NULL pointer argument");
+  for (int i = 0; i < n; ++i) {
+    if (index[i] < 0) return set_error(MOE_EINVAL, "index[%d]=%d < 0", i, index[i]);
+    const moe_apq_block& b = desc[i];
+    if (b.q < 1 || b.q > 8) return set_error(MOE_EINVAL, "desc[%d]: q=%d outside 1..8", i, b.q);
+    if (b.rows <= 0 || b.cols <= 0 || b.rows % kRowPanel || b.cols % kColChunk)
+      return set_error(MOE_EINVAL, "desc[%d]: need rows %% 64 == 0 and cols %% 128 == 0", i);
+  }
+  return launch_commit_blocks(table, index, desc, n, as_stream(stream));
+}
+
 int moe_workspace_routing(void* workspace, size_t ws_bytes, int T, int E, int H, int I, int k,
                           int I_shared, int32_t** topk_ids, float** topk_gates,
                           int32_t** expert_offsets, int32_t** sorted_pairs) {

@@ -174,6 +174,8 @@ int launch_decode_indices(const moe_apq_block& blk, uint8_t* idx_out, hipStream_
 int launch_routing_stats(const int32_t* offsets, const int32_t* pairs, const float* gates, int E,
                          const uint8_t* resident, unsigned long long* count, double* mass,
                          double* sums, hipStream_t stream);
+int launch_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
+                         hipStream_t stream);
 int launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace moeapq

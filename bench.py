@@ -320,6 +320,44 @@ def main():
                 "resident), from the routing results of a layer call; latency-bound single workgroup"}}
     log(f"[bench] routing statistics: {stats_us:.2f} us per call, m = {m:.4f}")
 
+    # width planning over every block of the layer (synthetic damage scores rising as the width
+    # falls, hot experts with a multiplier) to free a quarter of the weight bytes, on the host;
+    # then the commit of all of the layer's descriptors (same values) in stream order
+    blocks = [base.block(e, mm) for e in range(shape.E) for mm in (0, 1)]
+    if base.shared is not None:
+        blocks += [base.shared_block(0), base.shared_block(1)]
+    rng = np.random.default_rng(0)
+    qc = np.array([b.q for b in blocks], dtype=np.uint8)
+    dmg = np.cumsum(rng.random((len(blocks), 8))[:, ::-1], axis=1)[:, ::-1]
+    hot = np.concatenate([np.repeat(acc[0].cpu().numpy() > 0, 2), np.zeros(len(blocks) - 2 * shape.E, bool)])
+    mult = np.where(hot, 2.0, 1.0)
+    target = base.weight_bytes // 4
+    plan_args = (qc, np.minimum(qc, 2), [b.rows for b in blocks], [b.cols for b in blocks], dmg, mult, target)
+    apq.moe_plan_widths(*plan_args)
+    t0 = time.perf_counter()
+    reps = 200
+    for _ in range(reps):
+        q_plan, freed = apq.moe_plan_widths(*plan_args)
+    plan_us = (time.perf_counter() - t0) * 1e6 / reps
+    index = list(range(2 * shape.E))
+    apq.moe_commit_blocks(base.table, index, blocks[: 2 * shape.E], stream=stream)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(reps):
+        apq.moe_commit_blocks(base.table, index, blocks[: 2 * shape.E], stream=stream)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    commit_us = 1e3 * c0.elapsed_time(c1) / reps
+    next_rows["width_plan"] = {
+        "host_us_per_plan": round(plan_us, 2), "blocks": len(blocks), "target_bytes": int(target),
+        "bytes_freed": int(freed), "blocks_lowered": int((q_plan < qc).sum()),
+        "commit_us_per_call": round(commit_us, 3), "committed_descriptors": len(index),
+        "note": "greedy lowest damage per byte (synthetic scores, multiplier 2 on experts routed "
+                "in the timed calls) on the host; commit = stream-ordered page-table write"}
+    log(f"[bench] width plan: {plan_us:.1f} us on the host for {len(blocks)} blocks; "
+        f"commit of {len(index)} descriptors {commit_us:.2f} us")
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18   # fp32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)

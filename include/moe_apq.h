@@ -241,6 +241,42 @@ int moe_workspace_routing(void* workspace, size_t ws_bytes, int T, int E, int H,
                           int32_t** expert_offsets, int32_t** sorted_pairs);
 
 /*
+ * Commit new descriptors into the device weight page table, in stream order.
+ *
+ * Source: PagedWeight, Key Components 1 (a committed width q_i per block in the page table) and
+ * Key Components 3 (bit-width commits are applied only at safe boundaries, once a plan has run).
+ * Every call issued earlier on `stream` uses the old descriptors, every later one the new
+ * ones.  Lowering a block's width is a commit of the same planes pointer with a smaller q (the
+ * planes of width q' are the first q' planes) and the LUT of width q'; raising it is a commit
+ * after the missing planes and the new LUT have been copied in (e.g. an asynchronous copy from
+ * pinned host memory on another stream, which `stream` waits for with an event).
+ * table: device page table; index (host) [n]: entries to overwrite; desc (host) [n]: the new
+ * descriptors, copied by value into the launch (both host arrays may be reused on return).
+ * Nothing is allocated.  Errors: MOE_EINVAL (n < 0, NULL, negative index, q outside 1..8,
+ * rows % 64 or cols % 128), MOE_EHIP.
+ */
+int moe_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
+                      void* stream);
+
+/*
+ * Greedy bit-width plan (host, synchronous; no device access).
+ *
+ * Source: PagedWeight, Key Components 2 (quality-aware runtime planner: damage scores of
+ * bit-width reductions; when a memory target must be met, the reductions of lowest damage per
+ * byte saved are taken greedily; frequently routed experts get width floors and damage
+ * multipliers).  Readings: a reduction is one step q -> q-1 of one block, allowed while
+ * q-1 >= q_floor; its cost is mult * (damage(q-1) - damage(q)) / (bytes the step frees), in
+ * double; the cheapest is taken (ties: lower block index) until the bytes freed reach
+ * target_bytes or no step is left.  A block's bytes at width q: rows*cols*q/8 + rows*2^q*2.
+ * Inputs (host) [n]: q_cur (1..8), q_floor (1..q_cur), rows (% 64), cols (% 128), mult (> 0);
+ * damage [n*8]: damage[i*8 + w-1] = score of block i at width w.  Outputs: q_new [n],
+ * *bytes_saved.  Errors: MOE_EINVAL.
+ */
+int moe_plan_widths(int n, const uint8_t* q_cur, const uint8_t* q_floor, const int32_t* rows,
+                    const int32_t* cols, const float* damage, const float* mult,
+                    int64_t target_bytes, uint8_t* q_new, int64_t* bytes_saved);
+
+/*
  * Diagnostic: read `bytes` of device memory at `buf` once, with the access pattern that streams
  * fastest on this device (every wavefront reads one contiguous run in 1-KiB non-temporal loads,
  * 16 in flight), and XOR every 32-bit word of it into `*sink` (device, 4 bytes, stream-ordered

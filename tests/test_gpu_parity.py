@@ -401,3 +401,55 @@ def test_routing_stats_from_a_layer_calls_workspace():
     for a, b in zip(acc, ref):
         np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
     assert acc[2][0].item() == 0.0   # no resident mask: nothing substituted
+
+
+# ------------------------------------------------------------------------------------------
+# width commits in the page table (lower by a prefix of planes; restore by an async copy)
+# ------------------------------------------------------------------------------------------
+def test_width_commit_lower_then_restore_asynchronously():
+    """One routed block goes from q=6 to q=3 by a commit of the same planes (its first 3 are the
+    width-3 planes) with the width-3 LUT: the layer then matches the oracle at width 3.  Its
+    tail planes are cleared (as if freed) and copied back from pinned host memory on another
+    stream while the layer keeps running at width 3 (same output bit for bit); a commit ordered
+    after the copy's event brings width 6 back and the layer matches the oracle again."""
+    shape = wl.TINY.replace(H=256, E=6, I=256, k=2, T=12, name="width commit")
+    q6 = np.full((shape.E, 2), 6, dtype=np.uint8)
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape, q_override=q6)
+    ids, _ = oracle.route_topk(inputs.logits, shape.k)
+    e, m = int(ids[0, 0]), wl.GATE_UP
+    blk = dl.block(e, m)
+    idx8 = wl.gen_parent_indices(shape, e, m)
+
+    def check(qmap):
+        y, _ = _run_layer(shape, inputs, dl)
+        get, sh = gpu_layers.oracle_getters(shape, qmap)
+        ref = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh)
+        err = oracle.rel_l2(y, ref["y"])
+        say(f"  widths of expert {e}: {qmap[e]}: rel L2 {err:.2e}")
+        assert err <= LAYER_TOL
+        return y
+
+    lut3 = torch.from_numpy(np.ascontiguousarray(wl.gen_lut(shape, e, m, 3), dtype=np.float16)).to(DEV)
+    low = apq.ApqBlock(blk.planes, lut3.data_ptr(), blk.rows, blk.cols, 3, 6, apq.MOE_PAGE_GPU, 0, 0)
+    apq.moe_commit_blocks(dl.table, [2 * e + m], [low])
+    q3 = q6.copy()
+    q3[e, m] = 3
+    y3 = check(q3)
+
+    plane_bytes = blk.rows * blk.cols // 8
+    off = blk.planes - dl.arena.data_ptr()
+    tail = slice(off + 3 * plane_bytes, off + 6 * plane_bytes)
+    dl.arena[tail].zero_()
+    host_tail = torch.from_numpy(apq.moe_apq_pack(idx8, 6).view(np.uint8)[3 * plane_bytes: 6 * plane_bytes].copy()).pin_memory()
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dl.arena[tail].copy_(host_tail, non_blocking=True)
+        done.record(side)
+    y3b, _ = _run_layer(shape, inputs, dl)       # still width 3 while the copy runs
+    np.testing.assert_array_equal(y3b, y3)
+    torch.cuda.current_stream().wait_event(done)
+    apq.moe_commit_blocks(dl.table, [2 * e + m], [blk])
+    check(q6)

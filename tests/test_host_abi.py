@@ -133,3 +133,37 @@ def test_workspace_routing_addresses_lie_inside_the_workspace():
     assert lib.moe_workspace_routing(base, n, T, 0, H, I, k, Ish,
                                      *[ctypes.byref(p) for p in ptrs]) == apq.MOE_EINVAL
     assert lib.moe_routing_stats(None, None, None, T, k, E, None, None, None, None, None) == apq.MOE_EINVAL
+
+
+def test_native_width_planner_matches_oracle():
+    """moe_plan_widths (host C++, heap) against the oracle's plain greedy loop: same plan and
+    bytes saved, bit for bit, on random instances with floors, multipliers, ties and targets
+    from zero to unreachable."""
+    r = np.random.default_rng(8)
+    for trial in range(200):
+        n = int(r.integers(0, 12))
+        rows = r.choice([64, 128, 2816], n).astype(np.int32)
+        cols = r.choice([128, 1408, 2048], n).astype(np.int32)
+        qc = r.integers(1, 9, n).astype(np.uint8)
+        fl = np.minimum(qc, r.integers(1, 6, n)).astype(np.uint8)
+        dmg = np.cumsum(r.random((n, 8))[:, ::-1], axis=1)[:, ::-1].astype(np.float32)
+        if trial % 5 == 0 and n:
+            dmg[:] = 1.0          # all steps free: ties everywhere, decided by block index
+        mult = r.uniform(0.5, 3.0, n).astype(np.float32)
+        full = sum(oracle.block_bytes(rows[i], cols[i], qc[i]) - oracle.block_bytes(rows[i], cols[i], fl[i])
+                   for i in range(n))
+        target = int(r.integers(0, full + 4000)) if trial % 7 else full + 1
+        q, saved = apq.moe_plan_widths(qc, fl, rows, cols, dmg, mult, target)
+        q_ref, saved_ref = oracle.plan_widths(qc, fl, rows, cols, dmg.astype(np.float64),
+                                              mult.astype(np.float64), target)
+        np.testing.assert_array_equal(q, q_ref)
+        assert saved == saved_ref
+
+
+def test_native_width_planner_rejects_bad_arguments():
+    ok = dict(q_cur=[4], q_floor=[2], rows=[64], cols=[128], damage=np.zeros((1, 8)), mult=[1.0])
+    apq.moe_plan_widths(**ok, target_bytes=1)
+    for bad in (dict(q_floor=[5]), dict(q_cur=[9], q_floor=[1]), dict(rows=[60]), dict(cols=[100]),
+                dict(mult=[0.0])):
+        with pytest.raises(apq.MoeError):
+            apq.moe_plan_widths(**{**ok, **bad}, target_bytes=1)
