@@ -31,6 +31,9 @@ It is the plain, slow definition of what the layer computes, in float64 NumPy:
                     Misses Are Worth Waiting For?", Methodology: substituted gate mass).
 7. ``plan_widths``  the greedy width planner: lowest damage per byte saved until a memory
                     target is met (PagedWeight, Key Components 2).
+8. ``substitute`` / ``admit``  residency-aware substitution (fetch every miss, the 0.15 rule,
+                    the first-choice rule) and background admission ("Which Expert Misses
+                    Are Worth Waiting For?", Methodology).
 
 Readings where the pages are silent (all listed in the design notes of the repository):
 the parent width is 8 bits and plane p holds bit 7-p of the parent index, so the q-bit index
@@ -340,6 +343,70 @@ def plan_widths(q_cur, q_floor, rows, cols, damage, mult, target_bytes: int):
         saved += block_bytes(rows[best], cols[best], q[best]) - block_bytes(rows[best], cols[best], q[best] - 1)
         q[best] -= 1
     return np.array(q, dtype=np.uint8), saved
+
+
+# --------------------------------------------------------------------------------------------
+# 8. Residency-aware substitution policies and background admission
+# --------------------------------------------------------------------------------------------
+POLICY_FETCH_ALL = 0     # fetch every miss (the baseline)
+POLICY_GATE_RULE = 1     # fetch a miss if it is the first choice or its gate >= threshold
+POLICY_FIRST_CHOICE = 2  # fetch a miss only if it is the first choice
+
+
+def substitute(logits: np.ndarray, ids: np.ndarray, gates: np.ndarray, resident: np.ndarray,
+               policy: int, gate_threshold: float = 0.15):
+    """Substitution of non-resident experts ("Which Expert Misses Are Worth Waiting For?",
+    Methodology: fetch every miss; the 0.15 rule fetches a missed expert if it is the router's
+    first choice or its gate weight is >= 0.15 and substitutes the others; the first-choice rule
+    fetches only a missed first choice).  Readings where the page is silent: slots are taken in
+    order j = 0..k-1; a substituted slot gets the token's highest-logit resident expert that is
+    not already among its experts (ties: lower id), keeps its gate weight, and the token keeps
+    exactly k distinct experts; with no such expert left the miss is fetched.
+    Returns (new ids [T,k], missed [T,k] = original expert of a substituted slot else -1,
+    fetch [E] bool = a non-resident expert some token still uses)."""
+    T, k = ids.shape
+    E = logits.shape[1]
+    res = np.asarray(resident).reshape(-1) != 0
+    new = np.array(ids, dtype=np.int64, copy=True)
+    missed = np.full((T, k), -1, dtype=np.int64)
+    fetch = np.zeros(E, dtype=bool)
+    lg = np.asarray(logits, dtype=np.float64)
+    for t in range(T):
+        taken = set(int(v) for v in ids[t])
+        for j in range(k):
+            e = int(ids[t, j])
+            if res[e]:
+                continue
+            keep = (policy == POLICY_FETCH_ALL or
+                    (policy == POLICY_GATE_RULE and (j == 0 or gates[t, j] >= gate_threshold)) or
+                    (policy == POLICY_FIRST_CHOICE and j == 0))
+            cands = [c for c in range(E) if res[c] and c not in taken]
+            if keep or not cands:
+                fetch[e] = True
+                continue
+            best = min(cands, key=lambda c: (-lg[t, c], c))
+            new[t, j] = best
+            missed[t, j] = e
+            taken.add(best)
+    return new, missed, fetch
+
+
+def admit(missed: np.ndarray, gates: np.ndarray, acc: np.ndarray, threshold: float = 0.5):
+    """Background admission ("Which Expert Misses Are Worth Waiting For?", Methodology: the
+    substituted gate weight of an expert accumulates over time and the expert is admitted to
+    the cache once it reaches a threshold, e.g. 0.5).  Reading: per expert, the gates of this
+    call's slots substituted away from it are added in pair order (fp32, as the accumulator is
+    stored), then compared with the threshold; an admitted expert's accumulator restarts at 0.
+    Returns (new accumulators float32 [E], admitted bool [E])."""
+    acc = np.array(acc, dtype=np.float32, copy=True)
+    flat_m = np.asarray(missed).reshape(-1)
+    flat_g = np.asarray(gates, dtype=np.float32).reshape(-1)
+    for p in range(flat_m.size):
+        if flat_m[p] >= 0:
+            acc[flat_m[p]] = np.float32(acc[flat_m[p]] + flat_g[p])
+    admitted = acc >= np.float32(threshold)
+    acc[admitted] = 0.0
+    return acc, admitted
 
 
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:

@@ -477,3 +477,71 @@ def test_planner_invariants_and_exhaustive_optimality_of_each_step():
             done += oracle.block_bytes(rows[i], cols[i], cur[i]) - oracle.block_bytes(rows[i], cols[i], cur[i] - 1)
             cur[i] -= 1
         np.testing.assert_array_equal(cur, q)
+
+
+# ---- substitution policies and background admission ----------------------------------------
+def _subst_case(seed, T=20, E=24, k=4):
+    r = np.random.default_rng(seed)
+    logits = r.standard_normal((T, E))
+    ids, gates = oracle.route_topk(logits, k)
+    resident = r.random(E) < 0.4
+    return logits, ids, gates, resident
+
+
+def test_substitution_rules_keep_what_they_must_and_choose_the_best_resident():
+    """For every policy: all-resident changes nothing; every token keeps k distinct experts;
+    every substituted slot held a non-resident expert and now holds a resident one that is the
+    highest-logit resident expert not among the token's experts at that point (brute force over
+    the experts); the fetch set is exactly the non-resident experts still in use.  Policy
+    specifics: fetch-every-miss substitutes nothing; the first-choice rule never substitutes
+    slot 0; the gate rule never substitutes slot 0 or a gate >= 0.15."""
+    for seed in range(6):
+        logits, ids, gates, res = _subst_case(seed)
+        T, k = ids.shape
+        for pol in (oracle.POLICY_FETCH_ALL, oracle.POLICY_GATE_RULE, oracle.POLICY_FIRST_CHOICE):
+            same, none, _ = oracle.substitute(logits, ids, gates, np.ones(len(res)), pol)
+            np.testing.assert_array_equal(same, ids)
+            assert np.all(none == -1)
+            new, missed, fetch = oracle.substitute(logits, ids, gates, res, pol)
+            for t in range(T):
+                assert len(set(new[t])) == k
+                taken = set(ids[t])
+                for j in range(k):
+                    if missed[t, j] >= 0:
+                        assert missed[t, j] == ids[t, j] and not res[ids[t, j]] and res[new[t, j]]
+                        cands = [c for c in range(len(res)) if res[c] and c not in taken]
+                        assert new[t, j] == max(cands, key=lambda c: (logits[t, c], -c))
+                        taken.add(new[t, j])
+                    else:
+                        assert new[t, j] == ids[t, j]
+            used = {int(e) for e in new.ravel() if not res[e]}
+            assert set(np.flatnonzero(fetch)) == used
+            if pol == oracle.POLICY_FETCH_ALL:
+                assert np.all(missed == -1)
+            if pol in (oracle.POLICY_FIRST_CHOICE, oracle.POLICY_GATE_RULE):
+                assert np.all(missed[:, 0] == -1)
+            if pol == oracle.POLICY_GATE_RULE:
+                assert np.all(missed[gates >= 0.15] == -1)
+
+
+def test_substitution_hand_example_and_admission():
+    """One token, experts 0..4, logits [5, 4, 3, 2, 1], k = 3 -> ids (0, 1, 2); only experts 2
+    and 4 resident.  First-choice rule: slot 0 (expert 0) is fetched, slot 1 (expert 1) is
+    substituted by the best free resident expert, 4 (2 is already taken).  Admission: expert 1's
+    substituted gate accumulates across calls and is admitted when it reaches 0.5."""
+    logits = np.array([[5.0, 4.0, 3.0, 2.0, 1.0]])
+    ids, gates = oracle.route_topk(logits, 3)
+    np.testing.assert_array_equal(ids, [[0, 1, 2]])
+    res = np.array([0, 0, 1, 0, 1])
+    new, missed, fetch = oracle.substitute(logits, ids, gates, res, oracle.POLICY_FIRST_CHOICE)
+    np.testing.assert_array_equal(new, [[0, 4, 2]])
+    np.testing.assert_array_equal(missed, [[-1, 1, -1]])
+    np.testing.assert_array_equal(fetch, [True, False, False, False, False])
+    g1 = np.float32(gates[0, 1])              # e^-1 / (1 + e^-1 + e^-2) ~ 0.2447
+    assert abs(float(g1) - math.exp(-1) / (1 + math.exp(-1) + math.exp(-2))) < 1e-7
+    acc, adm = oracle.admit(missed, gates, np.zeros(5, np.float32))
+    assert acc[1] == g1 and not adm.any()
+    acc, adm = oracle.admit(missed, gates, acc)          # 0.489 < 0.5: not yet
+    assert acc[1] == np.float32(g1 + g1) and not adm.any()
+    acc, adm = oracle.admit(missed, gates, acc)          # 0.734 >= 0.5: admitted, restarts at 0
+    assert acc[1] == 0.0 and adm[1] and adm.sum() == 1
