@@ -31,6 +31,7 @@ EXPORTED = (
     "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
     "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_hbm_read_probe",
     "moe_routing_stats", "moe_workspace_routing", "moe_commit_blocks", "moe_plan_widths",
+    "moe_substitute",
     "moe_last_error",
 )
 
@@ -82,6 +83,7 @@ def _load():
         "moe_routing_stats": ([P, P, P, I, I, I, P, P, P, P, S], I),
         "moe_workspace_routing": ([P, Z, I, I, I, I, I, I, P, P, P, P], I),
         "moe_commit_blocks": ([P, P, P, I, S], I),
+        "moe_substitute": ([P, I, I, I, P, I, ctypes.c_float, P, P, P, P, P, ctypes.c_float, P, S], I),
         "moe_plan_widths": ([I, P, P, P, P, P, P, ctypes.c_int64, P, P], I),
         "moe_last_error": ([], ctypes.c_char_p),
     }
@@ -223,6 +225,22 @@ def moe_workspace_routing(workspace, T, E, H, I, k, I_shared=0) -> dict:
     TK = T * k
     return {"ids": view(ptrs[0], TK, torch.int32), "gates": view(ptrs[1], TK, torch.float32),
             "offsets": view(ptrs[2], E + 1, torch.int32), "pairs": view(ptrs[3], TK, torch.int32)}
+
+
+MOE_POLICY_FETCH_ALL, MOE_POLICY_GATE_RULE, MOE_POLICY_FIRST_CHOICE = 0, 1, 2
+
+
+def moe_substitute(logits, resident, policy, topk_ids, topk_gates, missed, fetch,
+                   gate_threshold=0.15, admit_mass=None, admit=None, admit_threshold=0.5,
+                   stream=None) -> None:
+    """Substitute non-resident routed experts in place in topk_ids (device tensors); see the
+    header for the policies, the outputs and the admission accumulators."""
+    T, E = logits.shape
+    k = topk_ids.shape[1] if topk_ids.dim() == 2 else topk_ids.numel() // max(T, 1)
+    _check("moe_substitute", _lib.moe_substitute(
+        _ptr(logits), T, E, k, _ptr(resident), int(policy), float(gate_threshold), _ptr(topk_ids),
+        _ptr(topk_gates), _ptr(missed), _ptr(fetch), None if admit_mass is None else _ptr(admit_mass),
+        float(admit_threshold), None if admit is None else _ptr(admit), _stream(stream)))
 
 
 def moe_commit_blocks(table, index, descs, stream=None) -> None:

@@ -307,6 +307,23 @@ int moe_routing_stats(const int32_t* expert_offsets, const int32_t* sorted_pairs
                               as_stream(stream));
 }
 
+int moe_substitute(const float* logits, int T, int E, int k, const uint8_t* resident, int policy,
+                   float gate_threshold, int32_t* topk_ids, const float* topk_gates,
+                   int32_t* missed, uint8_t* fetch, float* admit_mass, float admit_threshold,
+                   uint8_t* admit, void* stream) {
+  clear_error();
+  if (int rc = check_route_args(T, E, k)) return rc;
+  if (policy < MOE_POLICY_FETCH_ALL || policy > MOE_POLICY_FIRST_CHOICE)
+    return set_error(MOE_EINVAL, "unknown policy %d", policy);
+  if (!resident || !fetch) return set_error(MOE_EINVAL, "NULL pointer argument");
+  if ((admit_mass == nullptr) != (admit == nullptr))
+    return set_error(MOE_EINVAL, "admit_mass and admit must both be given or both be NULL");
+  if (T > 0 && (!logits || !topk_ids || !topk_gates || !missed))
+    return set_error(MOE_EINVAL, "NULL pointer argument");
+  return launch_substitute(logits, T, E, k, resident, policy, gate_threshold, topk_ids, topk_gates,
+                           missed, fetch, admit_mass, admit_threshold, admit, as_stream(stream));
+}
+
 int moe_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
                       void* stream) {
   clear_error();

@@ -176,6 +176,10 @@ int launch_routing_stats(const int32_t* offsets, const int32_t* pairs, const flo
                          double* sums, hipStream_t stream);
 int launch_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
                          hipStream_t stream);
+int launch_substitute(const float* logits, int T, int E, int k, const uint8_t* resident, int policy,
+                      float gate_threshold, int32_t* ids, const float* gates, int32_t* missed,
+                      uint8_t* fetch, float* admit_mass, float admit_threshold, uint8_t* admit,
+                      hipStream_t stream);
 int launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace moeapq

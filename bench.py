@@ -320,6 +320,28 @@ def main():
                 "resident), from the routing results of a layer call; latency-bound single workgroup"}}
     log(f"[bench] routing statistics: {stats_us:.2f} us per call, m = {m:.4f}")
 
+    # residency-aware substitution (the 0.15 rule, background admission) on the routing of the
+    # timed calls: the routed ids are copied first so that the layer's workspace stays intact
+    ids_copy = view["ids"].clone()
+    missed = torch.empty_like(ids_copy)
+    fetch = torch.empty(shape.E, dtype=torch.uint8, device=dev)
+    admit_mass = torch.zeros(shape.E, dtype=torch.float32, device=dev)
+    admit = torch.zeros(shape.E, dtype=torch.uint8, device=dev)
+    lg = logits.view(T, shape.E)
+    apq.moe_profile_start()
+    for _ in range(args.steps):
+        ids_copy.copy_(view["ids"])
+        apq.moe_substitute(lg, resident, apq.MOE_POLICY_GATE_RULE, ids_copy.view(T, shape.k), view["gates"],
+                           missed, fetch, admit_mass=admit_mass, admit=admit, stream=stream)
+    torch.cuda.synchronize()
+    sub_prof = apq.moe_profile_stop()
+    sub_us = 1e3 * sub_prof["substitute"][0] / sub_prof["substitute"][1]
+    next_rows["substitution"] = {
+        "us_per_call": round(sub_us, 3), "policy": "0.15 rule + background admission at 0.5",
+        "substituted_slots": int((missed >= 0).sum()), "fetched_experts": int(fetch.sum()),
+        "note": "one workgroup, a wavefront per token; a quarter of the experts resident"}
+    log(f"[bench] substitution: {sub_us:.2f} us per call")
+
     # width planning over every block of the layer (synthetic damage scores rising as the width
     # falls, hot experts with a multiplier) to free a quarter of the weight bytes, on the host;
     # then the commit of all of the layer's descriptors (same values) in stream order

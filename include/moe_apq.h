@@ -50,6 +50,11 @@ extern "C" {
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_TOKENS 65536
 
+/* Substitution policies of moe_substitute ("Which Expert Misses Are Worth Waiting For?"). */
+#define MOE_POLICY_FETCH_ALL 0     /* fetch every miss (no substitution)                     */
+#define MOE_POLICY_GATE_RULE 1     /* fetch a miss if first choice or gate >= gate_threshold */
+#define MOE_POLICY_FIRST_CHOICE 2  /* fetch a miss only if it is the first choice            */
+
 /* Page states of the weight page table (PagedWeight, Key Components 1). */
 #define MOE_PAGE_GPU 0
 #define MOE_PAGE_CPU 1
@@ -239,6 +244,32 @@ int moe_routing_stats(const int32_t* expert_offsets, const int32_t* sorted_pairs
 int moe_workspace_routing(void* workspace, size_t ws_bytes, int T, int E, int H, int I, int k,
                           int I_shared, int32_t** topk_ids, float** topk_gates,
                           int32_t** expert_offsets, int32_t** sorted_pairs);
+
+/*
+ * Residency-aware substitution of routed experts, and background admission.
+ *
+ * Source: "Which Expert Misses Are Worth Waiting For?", Methodology: a routed expert that is not
+ * GPU-resident (a miss) is fetched or substituted by a resident expert according to a policy
+ * (MOE_POLICY_*: fetch every miss; the 0.15 rule -- fetch a miss if it is the router's first
+ * choice or its gate weight is >= gate_threshold, e.g. 0.15; the first-choice rule); background
+ * admission accumulates an expert's substituted gate weight over calls and admits it to the
+ * cache once it reaches a threshold (e.g. 0.5).  Readings: slots are processed in order j =
+ * 0..k-1; a substituted slot gets the token's highest-logit resident expert not already among
+ * its experts (ties: lower id), keeps its gate weight, and each token keeps exactly k distinct
+ * experts; a miss with no such expert left is fetched.  Admission adds the gates of the slots
+ * substituted away from each expert in pair order (fp32), admits at the threshold and restarts
+ * the accumulator at 0.  Runs between moe_route_topk and moe_group_by_expert.
+ * Device arguments: logits fp32 [T,E] (finite); resident uint8 [E] (0 = not resident);
+ * topk_ids int32 [T,k] (in: routing, out: after substitution); topk_gates fp32 [T,k] (read);
+ * missed int32 [T,k] (out: the original expert of a substituted slot, else -1); fetch uint8 [E]
+ * (out: 1 = a non-resident expert still routed, to be fetched).  admit_mass float [E]
+ * (accumulators, in/out) and admit uint8 [E] (out: admitted this call): both NULL for no
+ * admission.  Errors: MOE_EINVAL (bad T/E/k, policy, NULL), MOE_EUNSUPPORTED (bounds).
+ */
+int moe_substitute(const float* logits, int T, int E, int k, const uint8_t* resident, int policy,
+                   float gate_threshold, int32_t* topk_ids, const float* topk_gates,
+                   int32_t* missed, uint8_t* fetch, float* admit_mass, float admit_threshold,
+                   uint8_t* admit, void* stream);
 
 /*
  * Commit new descriptors into the device weight page table, in stream order.

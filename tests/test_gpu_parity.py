@@ -453,3 +453,79 @@ def test_width_commit_lower_then_restore_asynchronously():
     torch.cuda.current_stream().wait_event(done)
     apq.moe_commit_blocks(dl.table, [2 * e + m], [blk])
     check(q6)
+
+
+# ------------------------------------------------------------------------------------------
+# residency-aware substitution and background admission
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("policy", [0, 1, 2], ids=["fetch-all", "gate-rule", "first-choice"])
+@pytest.mark.parametrize("T,E,k", [(24, 32, 4), (64, 512, 10), (9, 1024, 32), (16, 60, 4), (3, 5, 3)])
+def test_substitution_and_admission_bit_exact(policy, T, E, k):
+    """Substituted ids, the missed and fetch outputs and three calls of background admission
+    match the oracle bit for bit.  The oracle takes the GPU's fp32 gates and the fp32 threshold,
+    so the 0.15 decision is made in the kernel's precision on both sides."""
+    say(f"substitute policy={policy} T={T} E={E} k={k}")
+    r = np.random.default_rng(policy * 1000 + T + E + k)
+    logits = r.standard_normal((T, E)).astype(np.float32)
+    logits[:, 2] += 2.0
+    resident = (r.random(E) < 0.3).astype(np.uint8)
+    thr = float(np.float32(0.15))
+    lt = _t(logits)
+    acc = torch.zeros(E, dtype=torch.float32, device=DEV)
+    adm = torch.zeros(E, dtype=torch.uint8, device=DEV)
+    acc_ref = np.zeros(E, np.float32)
+    for call in range(3):
+        ids, gates = _route_gpu(logits, k)
+        ids0 = ids.cpu().numpy()
+        missed = torch.empty((T, k), dtype=torch.int32, device=DEV)
+        fetch = torch.empty(E, dtype=torch.uint8, device=DEV)
+        apq.moe_substitute(lt, _t(resident), policy, ids, gates, missed, fetch, gate_threshold=thr,
+                           admit_mass=acc, admit=adm)
+        torch.cuda.synchronize()
+        g = gates.cpu().numpy()
+        new_ref, missed_ref, fetch_ref = oracle.substitute(logits, ids0, g.astype(np.float64), resident,
+                                                           policy, gate_threshold=thr)
+        np.testing.assert_array_equal(ids.cpu().numpy(), new_ref)
+        np.testing.assert_array_equal(missed.cpu().numpy(), missed_ref)
+        np.testing.assert_array_equal(fetch.cpu().numpy().astype(bool), fetch_ref)
+        acc_ref, adm_ref = oracle.admit(missed_ref, g, acc_ref)
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+        np.testing.assert_array_equal(adm.cpu().numpy().astype(bool), adm_ref)
+
+
+def test_substituted_layer_matches_oracle_on_substituted_routing():
+    """Route, substitute (first-choice rule, a third of the experts resident), group and run the
+    FFN through the component calls: the output equals the oracle's layer evaluated on the
+    substituted ids with the original gates."""
+    shape = wl.TINY.replace(H=256, E=12, I=256, k=3, T=10, name="substituted layer")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    T, E, k = shape.T, shape.E, shape.k
+    resident = (np.arange(E) % 3 == 0).astype(np.uint8)
+    ids, gates = _route_gpu(inputs.logits, k)
+    missed = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    fetch = torch.empty(E, dtype=torch.uint8, device=DEV)
+    apq.moe_substitute(_t(inputs.logits), _t(resident), apq.MOE_POLICY_FIRST_CHOICE, ids, gates,
+                       missed, fetch)
+    off, pairs, act, nact = _group_gpu(ids, E)
+    y = torch.empty((T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(T, E, shape.H, shape.I, k, 0), dtype=torch.uint8, device=DEV)
+    apq.moe_apq_ffn(dl.table, E, shape.H, shape.I, _t(inputs.x), k, off, pairs, act, nact, gates, y, ws)
+    apq.moe_check_device_error(ws)
+    sub_ids = ids.cpu().numpy()
+    g = gates.cpu().numpy().astype(np.float64)
+    assert (missed.cpu().numpy() >= 0).any()
+    get, _ = gpu_layers.oracle_getters(shape)
+    # the oracle layer on fixed routing: logits that select exactly sub_ids with gates g
+    ref = np.zeros((T, shape.H))
+    x64 = inputs.x.astype(np.float64)
+    for t in range(T):
+        for j in range(k):
+            e = int(sub_ids[t, j])
+            gi, gq, gl = get(e, wl.GATE_UP)
+            di, dq, dlut = get(e, wl.DOWN)
+            ref[t] += g[t, j] * oracle.expert_ffn(oracle.committed_index(gi, gq), gl,
+                                                  oracle.committed_index(di, dq), dlut, x64[t:t + 1])[0]
+    err = oracle.rel_l2(y.float().cpu().numpy().astype(np.float64), ref)
+    say(f"  substituted layer rel L2 {err:.2e}")
+    assert err <= LAYER_TOL
