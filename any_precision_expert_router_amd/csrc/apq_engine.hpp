@@ -974,18 +974,19 @@ struct Ring {
 };
 
 // Branch-free choice of the chunk a freed slot takes next: chunk w of the current item, else
-// chunk w - m of the next item, else (nothing left) a re-read of the chunk just consumed, which
-// hits in cache.
-MOE_INLINE void pick_refill(const Geo& cur, const Geo& nxt, bool cont, int v, int w, int m, Geo& g,
-                            int& k) {
+// chunk w - m of the next item, else (nothing left) a filler whose Q + 4 loads all read the
+// first 256 bytes of token 0's activation row.  That row is hot in cache, so a filler never
+// reaches HBM; re-reading a plane chunk instead would, because plane loads are non-temporal.
+MOE_INLINE void pick_refill(const Geo& cur, const Geo& nxt, bool cont, int w, int m, Geo& g, int& k) {
   const bool use_cur = w < cur.n;
   const bool use_nxt = !use_cur && cont && w >= m && (w - m) < nxt.n;
-  g.pbase = use_nxt ? nxt.pbase : cur.pbase;
-  g.plane_u4 = use_nxt ? nxt.plane_u4 : cur.plane_u4;
-  g.cb = use_nxt ? nxt.cb : cur.cb;
+  const bool filler = !use_cur && !use_nxt;
+  g.pbase = filler ? cur.xbase[0] : (use_nxt ? nxt.pbase : cur.pbase);
+  g.plane_u4 = filler ? 0 : (use_nxt ? nxt.plane_u4 : cur.plane_u4);
+  g.cb = filler ? 0 : (use_nxt ? nxt.cb : cur.cb);
 #pragma unroll
   for (int t = 0; t < kMaxTokGroup; ++t) g.xbase[t] = use_nxt ? nxt.xbase[t] : cur.xbase[t];
-  k = use_cur ? w : (use_nxt ? w - m : (v < cur.n ? v : 0));
+  k = use_cur ? w : (use_nxt ? w - m : 0);
 }
 
 // Table lookups of one 32-column word of ring slot s.
@@ -1064,7 +1065,12 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
   prefetch_lut_q<Q>(it, lane, wave, L);
   make_geo<MODE>(A, it, cur);
 #pragma unroll
-  for (int s = 0; s < D; ++s) R.issue(s, cur, s < cur.n ? s : 0);
+  for (int s = 0; s < D; ++s) {
+    Geo g;
+    int k;
+    pick_refill(cur, cur, false, s, D, g, k);
+    R.issue(s, g, k);
+  }
   while (true) {
     Item next;
     const int j = Qu.nxt;
@@ -1097,7 +1103,7 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
         if (v < cur.n) ring_chunk<Q>(R, s, cur.ng, lane4, acc);
         Geo g;
         int k;
-        pick_refill(cur, nxt, cont, v, v + D, m, g, k);
+        pick_refill(cur, nxt, cont, v + D, m, g, k);
         R.issue(s, g, k);
       }
     }
