@@ -127,6 +127,86 @@ def cpu_baseline(shape, inputs, budget_s: float):
     return statistics.median(times), len(times)
 
 
+MFMA_FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix-core peak
+
+
+def prefill_row(apq, torch, dev, steps: int, warmup: int, check: bool):
+    """The chunked-prefill row: one moe_layer_forward over 2048 tokens of the Qwen2-57B-A14B-shaped
+    layer (64 experts of intermediate 2560, top-8, widths {3,4,6,8}), where about 256 tokens meet
+    every expert and the tile kernels take their matrix-core branch.  Compute-bound: reported as
+    TFLOP/s of the layer's algorithmic flops 2*T*k*3*H*I against the fp16 MFMA peak."""
+    import gpu_layers
+    import oracle
+    shape = wl.QWEN2_57B_A14B.with_tokens(wl.QWEN2_PREFILL_TOKENS)
+    log(f"[bench] prefill row: {shape.name}, T={shape.T}: building weights")
+    inputs = wl.gen_layer_inputs(shape)
+    widths = wl.gen_widths(shape)
+    layer = gpu_layers.device_layer(shape, device=dev)
+    T = shape.T
+    logits = torch.from_numpy(inputs.logits).to(dev)
+    x = torch.from_numpy(inputs.x).to(dev)
+    y = torch.empty((T, shape.H), dtype=torch.float16, device=dev)
+    ws = torch.zeros(apq.moe_workspace_bytes(T, shape.E, shape.H, shape.I, shape.k, 0),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        apq.moe_layer_forward(logits, x, shape.E, shape.H, shape.I, shape.k, layer.table, y, ws,
+                              stream=stream)
+
+    errs = None
+    if check:
+        step()
+        apq.moe_check_device_error(ws)
+        get, _ = gpu_layers.oracle_getters(shape, cache_size=16)
+        tok = [T // 2]
+        ref = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, tokens=tok)
+        yc = y.float().cpu().numpy()
+        errs = [oracle.rel_l2(yc[t], ref["y"][t]) for t in tok]
+        log(f"[bench] prefill parity on tokens {tok}: rel L2 {['%.2e' % e for e in errs]}")
+        assert max(errs) <= 1e-3, errs
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    apq.moe_profile_start()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = apq.moe_profile_stop()
+    per_kernel = {k: 1e3 * v[0] / v[1] for k, v in prof.items()}
+    ids_ref, _ = oracle.route_topk(inputs.logits, shape.k)
+    planes_b, lut_b = gpu_layers.active_weight_bytes(shape, ids_ref, widths)
+    flops = 2.0 * T * shape.k * 3 * shape.H * shape.I
+    gu_flops = 2.0 * T * shape.k * 2 * shape.I * shape.H
+    gu_us = per_kernel["apq_gate_up_silu"]
+    gu_tf = gu_flops / (gu_us * 1e-6) / 1e12
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"[bench] prefill: {us:.1f} us per layer, {tf:.1f} TFLOP/s; gate_up {gu_us:.1f} us = {gu_tf:.1f} TFLOP/s")
+    del layer, ws
+    torch.cuda.empty_cache()
+    return {
+        "workload": shape.name, "tokens": T, "us_per_layer": round(us, 2),
+        "TFLOPs": round(tf, 2), "flops_per_layer": flops,
+        "weight_GBs": round((planes_b + lut_b) / (us * 1e-6) / 1e9, 1),
+        "per_kernel_us": {k: round(v, 3) for k, v in per_kernel.items()},
+        "roofline": {"bound": "mfma", "kernel": "apq_gate_up_silu", "achieved": round(gu_tf, 2),
+                     "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / MFMA_FP16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_launch": gu_flops, "avg_launch_us": round(gu_us, 3)},
+        "parity_rel_l2": errs, "steps": steps,
+        "timing": f"{steps} eager calls between HIP events after {warmup} warmup calls; "
+                  "weights (1.25 GB) exceed the last-level cache",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +221,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed runs of --steps calls each (eager and graph); the median is reported")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the 2048-token chunked-prefill row (matrix-core path)")
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one device copy of this many MiB: the known-size "
                          "dispatch that calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -380,6 +463,10 @@ def main():
     log(f"[bench] width plan: {plan_us:.1f} us on the host for {len(blocks)} blocks; "
         f"commit of {len(index)} descriptors {commit_us:.2f} us")
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_row(apq, torch, dev, args.prefill_steps, 2, not args.no_check)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18   # fp32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -424,6 +511,7 @@ def main():
                   "(median of as many runs)",
         "graph_replay": graph,
         "next_rows": next_rows,
+        "prefill_row": prefill,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
