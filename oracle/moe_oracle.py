@@ -34,6 +34,9 @@ It is the plain, slow definition of what the layer computes, in float64 NumPy:
 8. ``substitute`` / ``admit``  residency-aware substitution (fetch every miss, the 0.15 rule,
                     the first-choice rule) and background admission ("Which Expert Misses
                     Are Worth Waiting For?", Methodology).
+9. ``lynx_bins`` / ``lynx_remap``  confidence bins from the top-logit gap and batch-aware
+                    remapping of low-affinity slots onto the critical expert set (LYNX, 2.2
+                    System Components).
 
 Readings where the pages are silent (all listed in the design notes of the repository):
 the parent width is 8 bits and plane p holds bit 7-p of the parent index, so the q-bit index
@@ -407,6 +410,72 @@ def admit(missed: np.ndarray, gates: np.ndarray, acc: np.ndarray, threshold: flo
     admitted = acc >= np.float32(threshold)
     acc[admitted] = 0.0
     return acc, admitted
+
+
+def lynx_bins(logits: np.ndarray, ids: np.ndarray, bin_width: float):
+    """AffinityBinning (LYNX, 2.2 System Components, confidence analyser: each token's router
+    confidence, taken from the gap between its top-ranked logits, is cut into bins whose width
+    and count follow from the sparsity ratio k/N alone).  Readings where the page is silent:
+    confidence c_t = l(ids[t,0]) - l(ids[t,1]), the gap between the token's two best logits,
+    as one fp32 subtraction; bin width w = k/N (fp32, passed in) and ceil(N/k) bins, so
+    b_t = min(floor(c_t / w), ceil(N/k) - 1) with the quotient rounded once to fp32; a token in
+    bin b keeps its first min(k, b + 1) slots as critical assignments.  For k = 1 every slot is
+    critical.  Returns (confidence float32 [T], bin int [T], kept slots int [T])."""
+    T, k = ids.shape
+    E = logits.shape[1]
+    lg = np.asarray(logits, dtype=np.float32)
+    w = np.float32(bin_width)
+    nbins = -(-E // k)
+    conf = np.zeros(T, dtype=np.float32)
+    bins = np.full(T, nbins - 1, dtype=np.int64)
+    keep = np.full(T, k, dtype=np.int64)
+    if k < 2:
+        return conf, bins, keep
+    for t in range(T):
+        c = np.float32(lg[t, ids[t, 0]] - lg[t, ids[t, 1]])
+        conf[t] = c
+        q = np.float32(c / w)
+        b = min(int(np.floor(q)), nbins - 1)
+        bins[t] = b
+        keep[t] = min(k, b + 1)
+    return conf, bins, keep
+
+
+def lynx_remap(logits: np.ndarray, ids: np.ndarray, bin_width: float):
+    """Batch-aware expert remapping (LYNX, 2.2 System Components, expert remapper: low-affinity
+    token-expert assignments are redirected to the surviving critical set of experts; every
+    token still activates exactly k experts while the batch activates fewer distinct ones).
+    Readings: the critical set is the set of experts of the critical assignments of every token
+    (its first ``keep`` slots, ``lynx_bins``); a non-critical slot whose expert is outside the
+    critical set takes the token's highest-logit critical expert not already among its experts
+    (ties: lower id), slots taken in order j = 0..k-1, and keeps its gate weight; with no such
+    expert left the slot keeps its own expert.
+    Returns (new ids [T,k], remapped [T,k] = original expert of a remapped slot else -1,
+    critical [E] bool)."""
+    T, k = ids.shape
+    E = logits.shape[1]
+    _, _, keep = lynx_bins(logits, ids, bin_width)
+    critical = np.zeros(E, dtype=bool)
+    for t in range(T):
+        for j in range(int(keep[t])):
+            critical[int(ids[t, j])] = True
+    lg = np.asarray(logits, dtype=np.float64)
+    new = np.array(ids, dtype=np.int64, copy=True)
+    remapped = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        taken = set(int(v) for v in ids[t])
+        for j in range(int(keep[t]), k):
+            e = int(ids[t, j])
+            if critical[e]:
+                continue
+            cands = [c for c in range(E) if critical[c] and c not in taken]
+            if not cands:
+                continue
+            best = min(cands, key=lambda c: (-lg[t, c], c))
+            new[t, j] = best
+            remapped[t, j] = e
+            taken.add(best)
+    return new, remapped, critical
 
 
 def rel_l2(a: np.ndarray, ref: np.ndarray) -> float:

@@ -545,3 +545,92 @@ def test_substitution_hand_example_and_admission():
     assert acc[1] == np.float32(g1 + g1) and not adm.any()
     acc, adm = oracle.admit(missed, gates, acc)          # 0.734 >= 0.5: admitted, restarts at 0
     assert acc[1] == 0.0 and adm[1] and adm.sum() == 1
+
+
+def test_lynx_hand_example():
+    """Three tokens over experts 0..5, k = 2, so the bin width is k/N = 1/3 (fp32) and there are
+    3 bins.  Token 0: logits (2, 1, ...) -> ids (0, 1), gap 1 -> bin 2 -> both slots critical.
+    Token 1: ids (2, 3), gap 0.125 -> bin 0 -> only slot 0 critical; expert 3 is outside the
+    critical set {0, 1, 2, 4}, so slot 1 takes the best free critical expert, 0 (logit 0.5).
+    Token 2: ids (4, 5), gap 0.25 -> bin 0; slot 1 (expert 5) takes expert 1 (logit 0.25).
+    The batch goes from 6 distinct experts to 4."""
+    logits = np.array([[2.0, 1.0, 0.5, 0.0, -1.0, -1.0],
+                       [0.5, -1.0, 3.0, 2.875, 0.0, -1.0],
+                       [-1.0, 0.25, -1.0, -1.0, 1.5, 1.25]], dtype=np.float32)
+    ids, _ = oracle.route_topk(logits, 2)
+    np.testing.assert_array_equal(ids, [[0, 1], [2, 3], [4, 5]])
+    w = np.float32(2) / np.float32(6)
+    conf, bins, keep = oracle.lynx_bins(logits, ids, w)
+    np.testing.assert_array_equal(conf, np.float32([1.0, 0.125, 0.25]))
+    np.testing.assert_array_equal(bins, [2, 0, 0])
+    np.testing.assert_array_equal(keep, [2, 1, 1])
+    new, remapped, critical = oracle.lynx_remap(logits, ids, w)
+    np.testing.assert_array_equal(new, [[0, 1], [2, 0], [4, 1]])
+    np.testing.assert_array_equal(remapped, [[-1, -1], [-1, 3], [-1, 5]])
+    np.testing.assert_array_equal(critical, [True, True, True, False, True, False])
+    assert len(set(ids.ravel())) == 6 and len(set(new.ravel())) == 4
+
+
+def test_lynx_bin_boundaries_and_quotient_rounding():
+    """A gap equal to the bin width lands in bin 1, the next fp32 value below it in bin 0; the
+    clamp puts very large gaps in the last bin, ceil(N/k) - 1.  The fp32 quotient equals the
+    double quotient rounded once to fp32 (exact for fp32 operands), on random gaps."""
+    E, k = 6, 2
+    w = np.float32(k) / np.float32(E)
+    below = np.nextafter(w, np.float32(0))
+    logits = np.full((3, E), -5.0, dtype=np.float32)
+    logits[0, 0], logits[0, 1] = w, 0.0
+    logits[1, 0], logits[1, 1] = below, 0.0
+    logits[2, 0], logits[2, 1] = 100.0, 0.0
+    ids, _ = oracle.route_topk(logits, k)
+    conf, bins, keep = oracle.lynx_bins(logits, ids, w)
+    assert conf[0] == w and conf[1] == below
+    np.testing.assert_array_equal(bins, [1, 0, 2])
+    np.testing.assert_array_equal(keep, [2, 1, 2])
+    r = np.random.default_rng(5)
+    for _ in range(2000):
+        c = np.float32(abs(r.standard_normal()))
+        ww = np.float32(r.integers(1, 33)) / np.float32(r.integers(33, 1025))
+        assert np.float32(c / ww) == np.float32(float(c) / float(ww))
+
+
+def test_lynx_remap_invariants_and_brute_force_choice():
+    """Random batches: every token keeps k distinct experts; its first `keep` slots are
+    unchanged; a remapped slot held a non-critical expert and now holds the highest-logit
+    critical expert not among the token's experts at that point (brute force); a slot that is
+    not remapped is unchanged; the critical set is exactly the experts of the kept slots; the
+    batch never activates more distinct experts than before.  k = 1, and a bin width so small
+    that every token keeps all its slots, change nothing."""
+    for seed in range(8):
+        r = np.random.default_rng(100 + seed)
+        T, E, k = int(r.integers(1, 40)), int(r.integers(8, 80)), int(r.integers(2, 7))
+        logits = (r.standard_normal((T, E)) * 0.3).astype(np.float32)
+        ids, _ = oracle.route_topk(logits, k)
+        w = np.float32(k) / np.float32(E)
+        _, _, keep = oracle.lynx_bins(logits, ids, w)
+        new, remapped, critical = oracle.lynx_remap(logits, ids, w)
+        crit_ref = np.zeros(E, dtype=bool)
+        for t in range(T):
+            crit_ref[ids[t, :keep[t]]] = True
+        np.testing.assert_array_equal(critical, crit_ref)
+        for t in range(T):
+            assert len(set(new[t])) == k
+            np.testing.assert_array_equal(new[t, :keep[t]], ids[t, :keep[t]])
+            taken = set(ids[t])
+            for j in range(k):
+                if remapped[t, j] >= 0:
+                    assert j >= keep[t] and remapped[t, j] == ids[t, j] and not critical[ids[t, j]]
+                    cands = [c for c in range(E) if critical[c] and c not in taken]
+                    assert new[t, j] == max(cands, key=lambda c: (float(logits[t, c]), -c))
+                    taken.add(int(new[t, j]))
+                else:
+                    assert new[t, j] == ids[t, j]
+        assert len(set(new.ravel())) <= len(set(ids.ravel()))
+        if -(-E // k) >= k:   # the last bin keeps every slot
+            same, none, _ = oracle.lynx_remap(logits, ids, np.float32(1e-30))
+            np.testing.assert_array_equal(same, ids)
+            assert np.all(none == -1)
+        ids1, _ = oracle.route_topk(logits, 1)
+        one, none1, _ = oracle.lynx_remap(logits, ids1, w)
+        np.testing.assert_array_equal(one, ids1)
+        assert np.all(none1 == -1)
