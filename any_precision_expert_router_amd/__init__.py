@@ -31,7 +31,7 @@ EXPORTED = (
     "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
     "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_hbm_read_probe",
     "moe_routing_stats", "moe_workspace_routing", "moe_commit_blocks", "moe_plan_widths",
-    "moe_substitute",
+    "moe_substitute", "moe_lynx_remap",
     "moe_last_error",
 )
 
@@ -84,6 +84,7 @@ def _load():
         "moe_workspace_routing": ([P, Z, I, I, I, I, I, I, P, P, P, P], I),
         "moe_commit_blocks": ([P, P, P, I, S], I),
         "moe_substitute": ([P, I, I, I, P, I, ctypes.c_float, P, P, P, P, P, ctypes.c_float, P, S], I),
+        "moe_lynx_remap": ([P, I, I, I, ctypes.c_float, P, P, P, S], I),
         "moe_plan_widths": ([I, P, P, P, P, P, P, ctypes.c_int64, P, P], I),
         "moe_last_error": ([], ctypes.c_char_p),
     }
@@ -241,6 +242,20 @@ def moe_substitute(logits, resident, policy, topk_ids, topk_gates, missed, fetch
         _ptr(logits), T, E, k, _ptr(resident), int(policy), float(gate_threshold), _ptr(topk_ids),
         _ptr(topk_gates), _ptr(missed), _ptr(fetch), None if admit_mass is None else _ptr(admit_mass),
         float(admit_threshold), None if admit is None else _ptr(admit), _stream(stream)))
+
+
+def moe_lynx_remap(logits, topk_ids, remapped, critical, bin_width=None, stream=None) -> None:
+    """Remap low-confidence slots of topk_ids (device int32 [T,k], in place) onto the critical
+    expert set; remapped gets each remapped slot's original expert (else -1), critical [E] the
+    set.  bin_width defaults to k/E in fp32.  See the header for the readings."""
+    T, E = logits.shape
+    k = topk_ids.shape[1] if topk_ids.dim() == 2 else topk_ids.numel() // max(T, 1)
+    if bin_width is None:
+        import numpy as _np
+        bin_width = float(_np.float32(k) / _np.float32(E))
+    _check("moe_lynx_remap", _lib.moe_lynx_remap(
+        _ptr(logits), T, E, k, float(bin_width), _ptr(topk_ids), _ptr(remapped), _ptr(critical),
+        _stream(stream)))
 
 
 def moe_commit_blocks(table, index, descs, stream=None) -> None:

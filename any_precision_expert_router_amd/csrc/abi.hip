@@ -2,6 +2,7 @@
 // carving, launch sequencing on the caller's stream, the optional kernel timer and error
 // messages.  No entry point allocates, frees or reads device memory back (except the explicit
 // moe_check_device_error / moe_profile_stop helpers, which synchronise by contract).
+#include <cfloat>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -322,6 +323,17 @@ int moe_substitute(const float* logits, int T, int E, int k, const uint8_t* resi
     return set_error(MOE_EINVAL, "NULL pointer argument");
   return launch_substitute(logits, T, E, k, resident, policy, gate_threshold, topk_ids, topk_gates,
                            missed, fetch, admit_mass, admit_threshold, admit, as_stream(stream));
+}
+
+int moe_lynx_remap(const float* logits, int T, int E, int k, float bin_width, int32_t* topk_ids,
+                   int32_t* remapped, uint8_t* critical, void* stream) {
+  clear_error();
+  if (int rc = check_route_args(T, E, k)) return rc;
+  if (!(bin_width > 0.0f) || !(bin_width <= FLT_MAX))
+    return set_error(MOE_EINVAL, "bin_width must be positive and finite");
+  if (!critical) return set_error(MOE_EINVAL, "NULL pointer argument");
+  if (T > 0 && (!logits || !topk_ids || !remapped)) return set_error(MOE_EINVAL, "NULL pointer argument");
+  return launch_lynx_remap(logits, T, E, k, bin_width, topk_ids, remapped, critical, as_stream(stream));
 }
 
 int moe_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,

@@ -180,6 +180,8 @@ int launch_substitute(const float* logits, int T, int E, int k, const uint8_t* r
                       float gate_threshold, int32_t* ids, const float* gates, int32_t* missed,
                       uint8_t* fetch, float* admit_mass, float admit_threshold, uint8_t* admit,
                       hipStream_t stream);
+int launch_lynx_remap(const float* logits, int T, int E, int k, float bin_width, int32_t* ids,
+                      int32_t* remapped, uint8_t* critical, hipStream_t stream);
 int launch_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 }  // namespace moeapq

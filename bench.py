@@ -425,6 +425,31 @@ def main():
         "note": "one workgroup, a wavefront per token; a quarter of the experts resident"}
     log(f"[bench] substitution: {sub_us:.2f} us per call")
 
+    # LYNX batch-aware remapping of the timed calls' routing onto the critical expert set: the
+    # distinct experts (and so the weight bytes a layer call must read) before and after
+    ids_l = view["ids"].clone()
+    remapped = torch.empty_like(ids_l)
+    critical = torch.empty(shape.E, dtype=torch.uint8, device=dev)
+    apq.moe_profile_start()
+    for _ in range(args.steps):
+        ids_l.copy_(view["ids"])
+        apq.moe_lynx_remap(lg, ids_l.view(T, shape.k), remapped, critical, stream=stream)
+    torch.cuda.synchronize()
+    lynx_prof = apq.moe_profile_stop()
+    lynx_us = 1e3 * lynx_prof["lynx_remap"][0] / lynx_prof["lynx_remap"][1]
+    ids_after = ids_l.view(T, shape.k).cpu().numpy()
+    pb_after, lb_after = gpu_layers.active_weight_bytes(shape, ids_after, widths)
+    next_rows["lynx_remap"] = {
+        "us_per_call": round(lynx_us, 3),
+        "distinct_experts_before": int(len(np.unique(ids_ref))),
+        "distinct_experts_after": int(len(np.unique(ids_after))),
+        "remapped_slots": int((remapped >= 0).sum()),
+        "weight_bytes_before": int(weight_bytes), "weight_bytes_after": int(pb_after + lb_after),
+        "note": "AffinityBinning with bin width k/N on the top-2 logit gap; one workgroup, a "
+                "wavefront per token; weight bytes are those a layer call would read"}
+    log(f"[bench] LYNX remap: {lynx_us:.2f} us per call, distinct experts "
+        f"{len(np.unique(ids_ref))} -> {len(np.unique(ids_after))}")
+
     # width planning over every block of the layer (synthetic damage scores rising as the width
     # falls, hot experts with a multiplier) to free a quarter of the weight bytes, on the host;
     # then the commit of all of the layer's descriptors (same values) in stream order

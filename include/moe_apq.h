@@ -272,6 +272,31 @@ int moe_substitute(const float* logits, int T, int E, int k, const uint8_t* resi
                    uint8_t* admit, void* stream);
 
 /*
+ * Batch-aware expert remapping onto a critical expert set.
+ *
+ * Source: LYNX, 2.2 System Components: a confidence analyser cuts each token's router
+ * confidence, taken from the gap between the logits of its top-ranked experts, into bins whose
+ * width and count are set by the sparsity ratio k/N alone (AffinityBinning); an expert remapper
+ * redirects low-affinity token-expert assignments to the surviving critical set of experts, and
+ * every token still activates exactly k experts.  Readings: confidence c = l(slot 0) - l(slot 1)
+ * in fp32; bin b = min(floor(c / bin_width), ceil(E/k) - 1), at least 0, with the quotient an
+ * IEEE fp32 division; a token in bin b keeps its first min(k, b + 1) slots as critical
+ * assignments and the critical set is the union of their experts; each other slot whose expert
+ * is not critical takes the token's highest-logit critical expert not already among its experts
+ * (ties: lower id), slots in order j = 0..k-1, and keeps its gate weight (gates are not touched);
+ * with no such expert left it keeps its own.  Runs between moe_route_topk and
+ * moe_group_by_expert, like moe_substitute.
+ * Device arguments: logits fp32 [T,E] (finite); topk_ids int32 [T,k] (in: routing output in
+ * routing order; out: after remapping); remapped int32 [T,k] (out: the original expert of a
+ * remapped slot, else -1); critical uint8 [E] (out: 1 = expert in the critical set).  bin_width
+ * is a host scalar, normally (float)k / (float)E.  One workgroup; nothing is allocated.
+ * Errors: MOE_EINVAL (bad T/E/k, bin_width not positive and finite, NULL), MOE_EUNSUPPORTED
+ * (bounds), MOE_EHIP.
+ */
+int moe_lynx_remap(const float* logits, int T, int E, int k, float bin_width, int32_t* topk_ids,
+                   int32_t* remapped, uint8_t* critical, void* stream);
+
+/*
  * Commit new descriptors into the device weight page table, in stream order.
  *
  * Source: PagedWeight, Key Components 1 (a committed width q_i per block in the page table) and

@@ -418,7 +418,7 @@ def lynx_bins(logits: np.ndarray, ids: np.ndarray, bin_width: float):
     and count follow from the sparsity ratio k/N alone).  Readings where the page is silent:
     confidence c_t = l(ids[t,0]) - l(ids[t,1]), the gap between the token's two best logits,
     as one fp32 subtraction; bin width w = k/N (fp32, passed in) and ceil(N/k) bins, so
-    b_t = min(floor(c_t / w), ceil(N/k) - 1) with the quotient rounded once to fp32; a token in
+    b_t = min(floor(c_t / w), ceil(N/k) - 1), at least 0, with the quotient rounded once to fp32; a token in
     bin b keeps its first min(k, b + 1) slots as critical assignments.  For k = 1 every slot is
     critical.  Returns (confidence float32 [T], bin int [T], kept slots int [T])."""
     T, k = ids.shape
@@ -435,7 +435,7 @@ def lynx_bins(logits: np.ndarray, ids: np.ndarray, bin_width: float):
         c = np.float32(lg[t, ids[t, 0]] - lg[t, ids[t, 1]])
         conf[t] = c
         q = np.float32(c / w)
-        b = min(int(np.floor(q)), nbins - 1)
+        b = max(0, min(int(np.floor(q)), nbins - 1))
         bins[t] = b
         keep[t] = min(k, b + 1)
     return conf, bins, keep

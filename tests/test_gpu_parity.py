@@ -529,3 +529,105 @@ def test_substituted_layer_matches_oracle_on_substituted_routing():
     err = oracle.rel_l2(y.float().cpu().numpy().astype(np.float64), ref)
     say(f"  substituted layer rel L2 {err:.2e}")
     assert err <= LAYER_TOL
+
+
+def _lynx_gpu(logits, ids, bin_width=None):
+    T, k = ids.shape
+    E = logits.shape[1]
+    remapped = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    critical = torch.empty(E, dtype=torch.uint8, device=DEV)
+    apq.moe_lynx_remap(_t(logits), ids, remapped, critical, bin_width=bin_width)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), remapped.cpu().numpy(), critical.cpu().numpy().astype(bool)
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(16, 60, 4, "matmul"), (64, 512, 10, "zipf"), (32, 8, 2, "matmul"),
+                                        (37, 1024, 32, "normal"), (5, 64, 1, "normal"),
+                                        (200, 128, 6, "flat"), (1, 3, 3, "normal")])
+def test_lynx_remap_bit_exact(T, E, k, kind):
+    """Remapped ids, the remapped-slot outputs and the critical set match the oracle bit for bit,
+    on the GPU's own routing (itself checked against the oracle).  The bin decision is an fp32
+    subtraction and an IEEE fp32 division on both sides.  Shapes: the Qwen1.5 and Qwen3-Next
+    (Zipf router) decode batches, a Mixtral-like 8-expert batch, the largest E and k, k = 1
+    (nothing remapped), low-confidence batches (small logit spread: many tokens in bin 0) and
+    k = E."""
+    say(f"lynx T={T} E={E} k={k} {kind}")
+    r = np.random.default_rng(T * 7 + E + k)
+    if kind == "matmul":
+        shape = wl.TINY.replace(H=512, E=E, k=k, T=T, router_std=0.02, name="lynx")
+        logits = wl.gen_layer_inputs(shape).logits
+    elif kind == "zipf":
+        logits = wl.gen_layer_inputs(wl.QWEN3_NEXT_80B_A3B).logits
+    elif kind == "flat":
+        logits = (r.standard_normal((T, E)) * 0.05).astype(np.float32)
+    else:
+        logits = r.standard_normal((T, E)).astype(np.float32)
+    ids, _ = _route_gpu(logits, k)
+    ids0 = ids.cpu().numpy()
+    ref_ids, _ = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(ids0, ref_ids)
+    w = np.float32(k) / np.float32(E)
+    new, remapped, critical = _lynx_gpu(logits, ids)
+    new_ref, rem_ref, crit_ref = oracle.lynx_remap(logits, ids0, w)
+    np.testing.assert_array_equal(new, new_ref)
+    np.testing.assert_array_equal(remapped, rem_ref)
+    np.testing.assert_array_equal(critical, crit_ref)
+    say(f"  distinct experts {len(set(ids0.ravel()))} -> {len(set(new.ravel()))}, "
+        f"remapped slots {(remapped >= 0).sum()}")
+
+
+def test_lynx_hand_example_and_bin_boundaries_on_gpu():
+    """The oracle's hand example (6 -> 4 distinct experts) and a gap exactly at the bin width
+    (bin 1) next to the fp32 value just below it (bin 0), through the kernel."""
+    logits = np.array([[2.0, 1.0, 0.5, 0.0, -1.0, -1.0],
+                       [0.5, -1.0, 3.0, 2.875, 0.0, -1.0],
+                       [-1.0, 0.25, -1.0, -1.0, 1.5, 1.25]], dtype=np.float32)
+    ids, _ = _route_gpu(logits, 2)
+    new, remapped, critical = _lynx_gpu(logits, ids)
+    np.testing.assert_array_equal(new, [[0, 1], [2, 0], [4, 1]])
+    np.testing.assert_array_equal(remapped, [[-1, -1], [-1, 3], [-1, 5]])
+    np.testing.assert_array_equal(critical, [True, True, True, False, True, False])
+    w = np.float32(2) / np.float32(6)
+    lg = np.full((2, 6), -5.0, dtype=np.float32)
+    lg[0, 0], lg[0, 1], lg[0, 2] = w, 0.0, -0.5
+    lg[1, 3], lg[1, 4], lg[1, 2] = np.nextafter(w, np.float32(0)), 0.0, -0.25
+    ids, _ = _route_gpu(lg, 2)
+    ids0 = ids.cpu().numpy()
+    new, remapped, critical = _lynx_gpu(lg, ids)
+    new_ref, rem_ref, crit_ref = oracle.lynx_remap(lg, ids0, w)
+    _, bins, _ = oracle.lynx_bins(lg, ids0, w)
+    np.testing.assert_array_equal(bins, [1, 0])
+    np.testing.assert_array_equal(new, new_ref)
+    np.testing.assert_array_equal(remapped, rem_ref)
+    np.testing.assert_array_equal(critical, crit_ref)
+
+
+def test_lynx_remapped_layer_matches_oracle():
+    """Route, remap (LYNX), group and run the FFN through the component calls: the output equals
+    the oracle's layer evaluated on the remapped ids with the original gates."""
+    shape = wl.TINY.replace(H=256, E=16, I=256, k=4, T=12, router_std=0.01, name="lynx layer")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    T, E, k = shape.T, shape.E, shape.k
+    ids, gates = _route_gpu(inputs.logits, k)
+    new, remapped, _ = _lynx_gpu(inputs.logits, ids)
+    assert (remapped >= 0).any()
+    off, pairs, act, nact = _group_gpu(ids, E)
+    y = torch.empty((T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(T, E, shape.H, shape.I, k, 0), dtype=torch.uint8, device=DEV)
+    apq.moe_apq_ffn(dl.table, E, shape.H, shape.I, _t(inputs.x), k, off, pairs, act, nact, gates, y, ws)
+    apq.moe_check_device_error(ws)
+    g = gates.cpu().numpy().astype(np.float64)
+    get, _ = gpu_layers.oracle_getters(shape)
+    ref = np.zeros((T, shape.H))
+    x64 = inputs.x.astype(np.float64)
+    for t in range(T):
+        for j in range(k):
+            e = int(new[t, j])
+            gi, gq, gl = get(e, wl.GATE_UP)
+            di, dq, dlut = get(e, wl.DOWN)
+            ref[t] += g[t, j] * oracle.expert_ffn(oracle.committed_index(gi, gq), gl,
+                                                  oracle.committed_index(di, dq), dlut, x64[t:t + 1])[0]
+    err = oracle.rel_l2(y.float().cpu().numpy().astype(np.float64), ref)
+    say(f"  LYNX-remapped layer rel L2 {err:.2e}")
+    assert err <= LAYER_TOL

@@ -89,6 +89,14 @@ def test_argument_validation_happens_before_any_launch():
                            fake, None, 0, None) == apq.MOE_EWORKSPACE
     assert lib.moe_layer_forward(fake, fake, 0, 8, 128, 256, 2, fake, None, 0, None, 0, fake, None, 0,
                                  None) == apq.MOE_OK                                     # T = 0
+    # LYNX remap: bin width must be positive and finite; outputs must be given
+    assert lib.moe_lynx_remap(fake, 4, 8, 2, 0.0, fake, fake, fake, None) == apq.MOE_EINVAL
+    assert lib.moe_lynx_remap(fake, 4, 8, 2, float("nan"), fake, fake, fake, None) == apq.MOE_EINVAL
+    assert lib.moe_lynx_remap(fake, 4, 8, 2, float("inf"), fake, fake, fake, None) == apq.MOE_EINVAL
+    assert lib.moe_lynx_remap(fake, 4, 8, 2, 0.25, fake, None, fake, None) == apq.MOE_EINVAL
+    assert lib.moe_lynx_remap(fake, 4, 8, 2, 0.25, fake, fake, None, None) == apq.MOE_EINVAL
+    assert lib.moe_lynx_remap(fake, 4, 8, 9, 0.25, fake, fake, fake, None) == apq.MOE_EINVAL    # k > E
+    assert lib.moe_lynx_remap(fake, 4, 2048, 2, 0.25, fake, fake, fake, None) == apq.MOE_EUNSUPPORTED
     blk = apq.ApqBlock(fake, fake, 64, 100, 4, 4, 0, 0, 0)
     assert lib.moe_apq_decode_indices(apq.ctypes.byref(blk), fake, None) == apq.MOE_EINVAL
     blk = apq.ApqBlock(fake, fake, 64, 128, 9, 4, 0, 0, 0)
