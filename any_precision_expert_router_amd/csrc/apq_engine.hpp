@@ -900,11 +900,250 @@ MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) 
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Wide tiles (more tokens than one matrix-core group: prefill chunks, where an expert meets
+// hundreds of tokens).  The dense path above decodes the weights once per 16 tokens; here each
+// decode serves kWideTok tokens, so the decode work per token falls by kWideTok / 16.
+//
+// The four wavefronts take one 32-column word each of every 128-column chunk (wavefront w: word
+// w), so a wavefront needs the activations of its own 32 columns only: its LDS ring slot holds
+// [4 octets][kWideTok tokens][16 bytes] = 4 KiB, filled by buffer loads straight to LDS, and two
+// slots fit the same 8 KiB per wavefront as the dense ring.  A lane loads its row's 32-bit word
+// of each plane (the four wavefronts' loads of one 1-KiB run share its cache lines).
+// The decoded word gives the A operands of two 16-column k steps exactly as in the dense path
+// (one v_permlane32_swap per register: rows 0-31 and rows 32-63); B is 32 distinct tokens
+// (lane n < 32: token n's first octet of the step, lane 32 + n: its second), so every output
+// column is a real token: per k step, 2 MFMAs per 32-token tile.  Each wavefront holds partial
+// sums over its quarter of the columns; they are reduced across wavefronts in LDS, one 32-token
+// tile at a time, through the drained rings.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWideTok = 64;                                      // tokens per pass
+constexpr int kWideTiles = kWideTok / 32;                         // 32-token MFMA tiles
+constexpr uint32_t kWideSlotBytes = 4 * kWideTok * 16;            // 4 octets x tokens x 16 B
+static_assert(2 * kWideSlotBytes == kXWaveBytes, "wide ring slots must fill the dense ring");
+
+template <int Q>
+struct WideStream {
+  static constexpr int D = 2;       // chunks in flight per wavefront
+  static constexpr int kDma = 4;    // one LDS load per octet (64 lanes = 64 tokens)
+  uint32_t buf[D][Q];               // this wavefront's plane word of the chunk, per plane
+  const AS_GLOBAL uint32_t* pbase;  // the lane's word in chunk 0 of plane 0
+  size_t plane_u32;                 // plane stride in 32-bit words
+  int cb, ce;                       // the item's chunks [cb, ce)
+  u32x4 xrsrc;                      // buffer resource of the activation rows
+  uint32_t rowoff;                  // per lane: byte offset of token (g0 + lane)'s word in row
+  uint32_t xring;                   // LDS address of this wavefront's ring
+  uint32_t bx;                      // per lane: B-operand address in slot 0, octet 0, tile 0
+
+  MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
+  // Activations of chunk c into slot `slot`, then its planes (loads issued unconditionally).
+  MOE_INLINE void issue(int slot, int c) {
+#pragma unroll
+    for (int i = 0; i < kDma; ++i)
+      lds_dma16(xring + slot * kWideSlotBytes + i * (kWideTok * 16), rowoff + i * 16u, xrsrc,
+                static_cast<uint32_t>(c) * 256u);
+#pragma unroll
+    for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u32 + static_cast<size_t>(c) * 256];
+  }
+  MOE_INLINE void prologue() {
+#pragma unroll
+    for (int s = 0; s < D; ++s) issue(s, clamp(cb + s));
+  }
+};
+
+// The staged activations of the chunk about to be consumed have landed: after them were issued
+// its own planes, the next chunk's activations and the next chunk's planes.
+template <int Q>
+MOE_INLINE void wide_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * Q + WideStream<Q>::kDma) : "memory");
+}
+
+// Geometry of the item for this wavefront and the activation rows of tokens [g0, g0 + ng).
+template <int MODE, int Q>
+MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng, WideStream<Q>& S) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int C = it.cols;
+  const int row = lane_row(it, lane);
+  const int nc4 = C / kColChunk;
+  // unit (panel, chunk 0, row) of plane 0, then this wavefront's 32-bit word inside it
+  S.pbase = gview<uint32_t>(it.planes) + (static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel)) * 4 + wave;
+  S.plane_u32 = static_cast<size_t>(it.rows) * C / 32;
+  S.cb = it.c0;
+  S.ce = it.c0 + it.nc;
+  const uint16_t* base;
+  size_t rows_total;
+  if constexpr (MODE == kGateUp) {
+    base = A.x;
+    rows_total = A.T;
+  } else if constexpr (MODE == kDown) {
+    base = it.shared ? A.act_shared : A.act;
+    rows_total = it.shared ? static_cast<size_t>(A.T) : static_cast<size_t>(A.T) * A.k;
+  } else {
+    base = A.x;
+    rows_total = A.T;
+  }
+  S.xrsrc = buffer_rsrc(base, static_cast<uint32_t>(rows_total * C * 2));
+  // token lane (tokens past ng re-read token g0's row; their columns are dropped)
+  const int tt = g0 + (lane < ng ? lane : 0);
+  int row_index;
+  if constexpr (MODE == kGateUp) {
+    row_index = it.shared ? tt : A.pairs[it.src_base + tt] / A.k;
+  } else if constexpr (MODE == kDown) {
+    row_index = it.shared ? tt : it.src_base + tt;
+  } else {
+    row_index = tt;
+  }
+  S.rowoff = static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) + static_cast<uint32_t>(wave) * 64u;
+  S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
+  S.bx = S.xring + static_cast<uint32_t>(lane >> 5) * (kWideTok * 16) + static_cast<uint32_t>(lane & 31) * 16u;
+}
+
+template <int Q>
+MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, f32x16 (&lo)[kWideTiles],
+                             f32x16 (&hi)[kWideTiles]) {
+  constexpr int D = WideStream<Q>::D;
+  for (int c0 = S.cb; c0 < S.ce; c0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      const int c = c0 + s;
+      if (c < S.ce) {
+        wide_wait<Q>();
+        uint32_t w[Q];
+#pragma unroll
+        for (int p = 0; p < Q; ++p) w[p] = S.buf[s][p];
+        uint32_t wv[16];
+        decode_word_dense<Q>(w, lane4, wv);
+        const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kWideSlotBytes;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          // k step st: octets 2 st and 2 st + 1 of the word (columns 16 st .. 16 st + 15)
+          uint32_t a1[4], a2[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(wv[8 * st + r], wv[8 * st + 4 + r], false, false);
+            a1[r] = sw[0];
+            a2[r] = sw[1];
+          }
+          const u32x4 va1 = {a1[0], a1[1], a1[2], a1[3]}, va2 = {a2[0], a2[1], a2[2], a2[3]};
+#pragma unroll
+          for (int g = 0; g < kWideTiles; ++g) {
+            const u32x4 b = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (kWideTok * 16) + g * 512);
+            lo[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va1),
+                                                          __builtin_bit_cast(half8_t, b), lo[g], 0, 0, 0);
+            hi[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va2),
+                                                          __builtin_bit_cast(half8_t, b), hi[g], 0, 0, 0);
+          }
+        }
+        S.issue(s, S.clamp(c + D));
+      }
+    }
+  }
+}
+
+// Reduce the four wavefronts' partial sums of one 32-token tile (tokens g0 + 32 g ..) and store
+// them.  D layout: lane l, register i holds row m = 8 (i / 4) + 4 (l / 32) + i % 4 of `lo`
+// (32 + m of `hi`) for token 32 g + l % 32.
+template <int MODE>
+MOE_INLINE void wide_reduce_tile(const KArgs& A, const Item& it, int g0, int ng, int g, f32x16& lo,
+                                 f32x16& hi, const Queue* Qu) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  float* ring = reinterpret_cast<float*>(reinterpret_cast<char*>(g_lds) + kXRingBase);
+  if (wave > 0) {
+    float* mine = ring + wave * (kXWaveBytes / 4);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      mine[i * 64 + lane] = lo[i];
+      mine[(16 + i) * 64 + lane] = hi[i];
+    }
+  }
+  if (Qu) queue_publish(*Qu);
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 1; w < kWavesPerTile; ++w) {
+      const float* other = ring + w * (kXWaveBytes / 4);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        lo[i] += other[i * 64 + lane];
+        hi[i] += other[(16 + i) * 64 + lane];
+      }
+    }
+    const int tok = 32 * g + (lane & 31);
+    const bool live = tok < ng;
+    uint16_t* act_dst = nullptr;
+    float* out_dst = nullptr;
+    float scale = 1.0f;
+    if (live) {
+      if constexpr (MODE == kGateUp) {
+        act_dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + tok) * A.I_shared + it.r0
+                            : A.act + static_cast<size_t>(it.src_base + g0 + tok) * A.I + it.r0;
+      } else if constexpr (MODE == kDown) {
+        if (it.shared) {
+          if (A.shared_scale) scale = A.shared_scale[g0 + tok];
+          out_dst = A.part_shared + (static_cast<size_t>(it.seg) * A.T + g0 + tok) * A.H;
+        } else {
+          const int p = A.pairs[it.src_base + g0 + tok];
+          scale = A.gates[p];
+          out_dst = A.part + (static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H;
+        }
+        out_dst += it.r0;
+      } else {
+        out_dst = A.y_plain + static_cast<size_t>(g0 + tok) * it.rows + it.r0;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if constexpr (MODE == kGateUp) {
+        if (live) act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(silu_mul(lo[i], hi[i])));
+      } else {
+        if (live) {
+          out_dst[m] = scale * lo[i];
+          out_dst[32 + m] = scale * hi[i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int MODE, int Q>
+MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  u32x4 L[kLutRegs];
+  prefetch_lut_q<Q>(it, lane, wave, L);
+  WideStream<Q> S;
+  make_wide_stream<MODE, Q>(A, it, 0, min(kWideTok, it.n), S);
+  S.prologue();
+  write_dense_table<Q>(L, lane, wave);
+  __syncthreads();
+  for (int g0 = 0; g0 < it.n; g0 += kWideTok) {
+    const int ng = min(kWideTok, it.n - g0);
+    if (g0 > 0) {
+      make_wide_stream<MODE, Q>(A, it, g0, ng, S);
+      S.prologue();
+    }
+    f32x16 lo[kWideTiles], hi[kWideTiles];
+#pragma unroll
+    for (int g = 0; g < kWideTiles; ++g) lo[g] = hi[g] = f32x16{};
+    wide_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, lo, hi);
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the ring's last (re-read) loads
+    const bool last = g0 + kWideTok >= it.n;
+#pragma unroll
+    for (int g = 0; g < kWideTiles; ++g)
+      if (32 * g < ng) wide_reduce_tile<MODE>(A, it, g0, ng, g, lo[g], hi[g], last && g == 0 ? &Qu : nullptr);
+  }
+}
+
 // A tile that does not stream (at least as many tokens as the dense threshold, or more than 4):
-// matrix-core path.
+// matrix-core path, wide when one 16-token pass would not hold its tokens.
 template <int MODE, int Q>
 MOE_INLINE void run_item(const KArgs& A, const Item& it, const Queue& Qu) {
-  run_item_dense<MODE, Q>(A, it, Qu);
+  if (it.n > kDenseGroup) run_item_wide<MODE, Q>(A, it, Qu);
+  else run_item_dense<MODE, Q>(A, it, Qu);
 }
 
 // ---------------------------------------------------------------------------------------------

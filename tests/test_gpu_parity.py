@@ -157,6 +157,26 @@ def test_gemv_matches_oracle(q, T, dense, C):
     assert oracle.rel_l2(y.cpu().numpy(), ref) <= 1e-5
 
 
+@pytest.mark.parametrize("q", range(1, 9))
+@pytest.mark.parametrize("T", [33, 64, 65, 130])
+def test_gemv_wide_passes_match_oracle(q, T):
+    """More tokens than one 16-token matrix-core pass: the wide path (64 tokens per decode of the
+    weights, 32-token MFMA tiles, one 32-column word of each chunk per wavefront).  Token counts
+    cover one partly used tile, exactly one pass, one token into a second pass and a ragged third
+    pass; C = 2176 gives 17 chunks (an odd count for the two-slot ring)."""
+    say(f"gemv wide q={q} T={T}")
+    R, C = 128, 2176
+    r = np.random.default_rng(q * 1000 + T)
+    idx8 = r.integers(0, 256, size=(R, C), dtype=np.uint8)
+    lut = (np.sort(r.standard_normal((R, 1 << q)), axis=1) * 0.02).astype(np.float16)
+    x = r.standard_normal((T, C)).astype(np.float16)
+    blk, keep = _upload_block(idx8, q, lut)
+    y = torch.empty((T, R), dtype=torch.float32, device=DEV)
+    apq.moe_apq_gemv(blk, _t(x), y)
+    ref = oracle.apq_matvec(oracle.committed_index(idx8, q), lut, x.astype(np.float64).T).T
+    assert oracle.rel_l2(y.cpu().numpy(), ref) <= 1e-5
+
+
 @pytest.mark.parametrize("dense", [1000, 1], ids=["valu", "mfma"])
 @pytest.mark.parametrize("q", range(1, 9))
 @pytest.mark.parametrize("C", [256, 2048])
@@ -259,6 +279,17 @@ def test_layer_many_tokens_on_one_expert(threshold, T):
     expert whose items loop over the 16-token groups."""
     shape = wl.TINY.replace(E=4, k=2, T=T, name="hot experts")
     _check_layer(shape, threshold=threshold)
+
+
+def test_layer_prefill_chunk_every_width_and_shared_expert():
+    """A prefill-sized call (530 tokens x top-2 = 1060 pairs, above the record split limit): every
+    routed expert and the shared expert meet far more than 16 tokens and run the wide
+    matrix-core path over passes of 64 tokens, at every width 1..8, with a shared-expert scale."""
+    shape = wl.TINY.replace(H=256, E=6, I=384, k=2, T=530, I_shared=256, q_shared=8,
+                            name="prefill chunk")
+    q = np.array([[1 + (2 * e + m) % 8 for m in range(2)] for e in range(shape.E)], dtype=np.uint8)
+    r = np.random.default_rng(11)
+    _check_layer(shape, q_override=q, shared_scale=r.uniform(-1, 2, size=shape.T))
 
 
 def test_layer_is_deterministic():
