@@ -39,6 +39,7 @@ WORKLOADS = {
     "qwen2_57b_a14b_t8": wl.QWEN2_57B_A14B.with_tokens(8),
     "qwen2_57b_a14b_t32": wl.QWEN2_57B_A14B.with_tokens(32),
     "qwen2_57b_a14b_t128": wl.QWEN2_57B_A14B.with_tokens(128),
+    "qwen2_57b_a14b_prefill2048": wl.QWEN2_57B_A14B.with_tokens(wl.QWEN2_PREFILL_TOKENS),
     "tiny": wl.TINY,
 }
 # the FFN kernel whose roofline the line reports, and the blocks (module) it reads
