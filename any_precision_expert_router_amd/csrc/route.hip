@@ -112,20 +112,26 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_topk_kernel(
 }
 
 constexpr int kGroupThreads = 1024;
-constexpr int kGroupMapBytes = 16384;  // LDS token x expert slot map per chunk
+constexpr int kGroupMapBytes = 16384;  // LDS of the stable placement (slot map or segment counters)
 
 struct GroupSmem {
   int32_t count[MOE_MAX_EXPERTS];
   int32_t wave_tot[2][kGroupThreads / 64];
-  uint8_t slot_map[kGroupMapBytes];
+  union {
+    uint8_t slot_map[kGroupMapBytes];     // small batches: token x expert slot map per chunk
+    int32_t seg_pos[kGroupMapBytes / 4];  // large batches: [segments][E] pair counts, then positions
+  };
   int32_t offsets[MOE_MAX_EXPERTS + 1];  // LDS copies of the grouping results for the records
   int32_t active[MOE_MAX_EXPERTS];
   int32_t n_active;
 };
 
 // Stable grouping by one workgroup of kGroupThreads threads.  `ids` may have been written by this
-// workgroup before a barrier.
-__device__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
+// workgroup before a barrier.  SEGMENTED picks the placement: a segmented counting sort (large
+// batches: every wavefront places its own run of tokens), or a token x expert slot map walked by
+// one thread per expert (small batches, where it measured faster).
+template <bool SEGMENTED>
+__device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ pairs, int32_t* __restrict__ active,
                            int32_t* __restrict__ n_active, GroupSmem& sm, int32_t* pairs_lds) {
   const int tid = threadIdx.x;
@@ -172,30 +178,75 @@ __device__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __r
   for (int e = tid; e < E; e += kGroupThreads)
     if (e >= n_act) active[e] = -1;
 
-  // stable placement, chunk by chunk over tokens: because the k experts of one token are
-  // distinct, a pair's rank inside its expert is the number of earlier tokens that picked it
-  int cursor = excl;
-  const int chunk = kGroupMapBytes / E > 0 ? kGroupMapBytes / E : 1;
-  for (int t0 = 0; t0 < T; t0 += chunk) {
-    const int tn = min(chunk, T - t0);
-    for (int i = tid; i < tn * E; i += kGroupThreads) sm.slot_map[i] = 0;
+  if constexpr (SEGMENTED) {
+    // stable placement by a segmented counting sort: the tokens are cut into S consecutive
+    // segments, one per wavefront; each wavefront counts its segment's pairs per expert, a
+    // per-expert prefix over the segments (starting at the expert's offset) gives each segment its
+    // first position, and each wavefront then walks its tokens in order.  Because the k experts
+    // of one token are distinct, the k lanes of a token never update the same position counter.
+    const int S = max(1, min(kGroupThreads / 64, static_cast<int>(kGroupMapBytes / (4 * E))));
+    const int seg_len = (T + S - 1) / S;
+    for (int i = tid; i < S * E; i += kGroupThreads) sm.seg_pos[i] = 0;
     __syncthreads();
-    for (int i = tid; i < tn * k; i += kGroupThreads) {
-      const int tt = i / k, j = i - tt * k;
-      sm.slot_map[tt * E + ids[(t0 + tt) * k + j]] = static_cast<uint8_t>(j + 1);
+    const int t_begin = min(T, wave * seg_len), t_end = min(T, t_begin + seg_len);
+    if (wave < S) {
+      for (int i = t_begin * k + lane; i < t_end * k; i += 64) atomicAdd(&sm.seg_pos[wave * E + ids[i]], 1);
     }
     __syncthreads();
-    if (tid < E && c > 0) {
-      for (int tt = 0; tt < tn; ++tt) {
-        const int s = sm.slot_map[tt * E + tid];
-        if (s) {
-          const int p = (t0 + tt) * k + (s - 1);
-          if (pairs_lds) pairs_lds[cursor] = p;
-          pairs[cursor++] = p;
+    if (tid < E) {
+      int run = excl;
+      for (int w = 0; w < S; ++w) {
+        const int n = sm.seg_pos[w * E + tid];
+        sm.seg_pos[w * E + tid] = run;
+        run += n;
+      }
+    }
+    __syncthreads();
+    if (wave < S && lane < k) {
+      constexpr int kBatch = 16;  // expert ids loaded ahead of the in-order placement
+      for (int t0 = t_begin; t0 < t_end; t0 += kBatch) {
+        int e[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) e[u] = t0 + u < t_end ? ids[(t0 + u) * k + lane] : 0;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (t0 + u < t_end) {
+            const int p = (t0 + u) * k + lane;
+            const int pos = sm.seg_pos[wave * E + e[u]];
+            sm.seg_pos[wave * E + e[u]] = pos + 1;
+            if (pairs_lds) pairs_lds[pos] = p;
+            pairs[pos] = p;
+          }
         }
       }
     }
     __syncthreads();
+  } else {
+    // stable placement, chunk by chunk over tokens: because the k experts of one token are
+    // distinct, a pair's rank inside its expert is the number of earlier tokens that picked it
+    int cursor = excl;
+    const int chunk = kGroupMapBytes / E > 0 ? kGroupMapBytes / E : 1;
+    for (int t0 = 0; t0 < T; t0 += chunk) {
+      const int tn = min(chunk, T - t0);
+      for (int i = tid; i < tn * E; i += kGroupThreads) sm.slot_map[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < tn * k; i += kGroupThreads) {
+        const int tt = i / k, j = i - tt * k;
+        sm.slot_map[tt * E + ids[(t0 + tt) * k + j]] = static_cast<uint8_t>(j + 1);
+      }
+      __syncthreads();
+      if (tid < E && c > 0) {
+        for (int tt = 0; tt < tn; ++tt) {
+          const int s = sm.slot_map[tt * E + tid];
+          if (s) {
+            const int p = (t0 + tt) * k + (s - 1);
+            if (pairs_lds) pairs_lds[cursor] = p;
+            pairs[cursor++] = p;
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -203,7 +254,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_by_expert_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ pairs, int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
   __shared__ GroupSmem sm;
-  group_body(ids, T, k, E, offsets, pairs, active, n_active, sm, nullptr);
+  group_body<true>(ids, T, k, E, offsets, pairs, active, n_active, sm, nullptr);
 }
 
 __device__ __forceinline__ bool block_valid(const moe_apq_block& b, int rows, int cols) {
@@ -318,7 +369,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_records_kernel(
                           s_gates + o);
   }
   __syncthreads();
-  group_body(s_ids, T, k, E, offsets, pairs, active, n_active, sm, s_pairs);
+  group_body<false>(s_ids, T, k, E, offsets, pairs, active, n_active, sm, s_pairs);
   __syncthreads();
   records_body(sm, s_pairs, s_gates, r);
 }
@@ -327,7 +378,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_records_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
     int32_t* __restrict__ active, int32_t* __restrict__ n_active, RecordArgs r) {
   __shared__ GroupSmem sm;
-  group_body(ids, r.T, r.k, r.E, offsets, pairs, active, n_active, sm, nullptr);
+  group_body<true>(ids, r.T, r.k, r.E, offsets, pairs, active, n_active, sm, nullptr);
   __syncthreads();
   records_body(sm, pairs, r.gates, r);
 }
