@@ -20,9 +20,13 @@
 //   * q >= 5 (SINGLE): byte = idx of one column; the row's 2^q-entry table returns one fp16.
 // Tables are stored entry-major with one 4-byte slot per lane ([entry][64 lanes]), so a lookup
 // is conflict-free whatever the indices, and the LDS address is one v_perm of the index byte
-// next to the lane offset.  The products use v_dot2_f32_f16 (two MACs, fp32 accumulate) against
-// the token activations, which are uniform across the wavefront and so read through the scalar
-// unit.  Weights are never expanded to a dense matrix in memory.
+// next to the lane offset.
+//
+// Products.  Tiles with at most 4 tokens stream: v_dot2c_f32_f16 (two MACs, fp32 accumulate)
+// against the token activations, broadcast across each 16-lane row by DPP.  Tiles with more
+// tokens use the matrix cores (v_mfma_f32_32x32x16_f16) on the decoded fp16 weights: the dense
+// branch takes 16 tokens per decode of the weights, the wide branch (prefill chunks) 64.
+// Weights are never expanded to a dense matrix in memory.
 #pragma once
 #include "internal.hpp"
 
