@@ -1195,15 +1195,16 @@ MOE_INLINE void make_geo(const KArgs& A, const Item& it, Geo& G) {
   }
 }
 
-template <int Q>
+// NT: activation rows the ring loads per chunk (1, 2 or 4: the stream's largest token count).
+template <int Q, int NT>
 struct Ring {
   static constexpr int D = ring_depth<Q>();
   u32x4 buf[D][Q];
-  u32x4 xbuf[D][kMaxTokGroup];
+  u32x4 xbuf[D][NT];
 
   // Chunk k (0-based within the wavefront's share) of geometry g into `slot` (compile-time).
-  // Every call issues exactly Q + 4 loads: unused token slots re-read token 0's activations, so
-  // the number of loads in flight never depends on run-time branches and the compiler's
+  // Every call issues exactly Q + NT loads: unused token slots re-read token 0's activations,
+  // so the number of loads in flight never depends on run-time branches and the compiler's
   // wait counts stay exact.
   MOE_INLINE void issue(int slot, const Geo& g, int k) {
     const size_t c = static_cast<size_t>(g.cb + k);
@@ -1212,12 +1213,12 @@ struct Ring {
 #pragma unroll
     for (int p = 0; p < Q; ++p) buf[slot][p] = __builtin_nontemporal_load(&g.pbase[p * g.plane_u4 + c * 64]);
 #pragma unroll
-    for (int t = 0; t < kMaxTokGroup; ++t) xbuf[slot][t] = g.xbase[t][c * 16];
+    for (int t = 0; t < NT; ++t) xbuf[slot][t] = g.xbase[t][c * 16];
   }
 };
 
 // Branch-free choice of the chunk a freed slot takes next: chunk w of the current item, else
-// chunk w - m of the next item, else (nothing left) a filler whose Q + 4 loads all read the
+// chunk w - m of the next item, else (nothing left) a filler whose Q + NT loads all read the
 // first 256 bytes of token 0's activation row.  That row is hot in cache, so a filler never
 // reaches HBM; re-reading a plane chunk instead would, because plane loads are non-temporal.
 MOE_INLINE void pick_refill(const Geo& cur, const Geo& nxt, bool cont, int w, int m, Geo& g, int& k) {
@@ -1233,8 +1234,8 @@ MOE_INLINE void pick_refill(const Geo& cur, const Geo& nxt, bool cont, int w, in
 }
 
 // Table lookups of one 32-column word of ring slot s.
-template <int Q, int JW>
-MOE_INLINE void ring_decode(const Ring<Q>& R, int s, uint32_t lane4, uint32_t (&wv)[16]) {
+template <int Q, int NT, int JW>
+MOE_INLINE void ring_decode(const Ring<Q, NT>& R, int s, uint32_t lane4, uint32_t (&wv)[16]) {
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = word_of(R.buf[s][p], JW);
@@ -1243,11 +1244,11 @@ MOE_INLINE void ring_decode(const Ring<Q>& R, int s, uint32_t lane4, uint32_t (&
 }
 
 // Products of one decoded 32-column word for the ng (<= 4) tokens of ring slot s.
-template <int Q, int JW>
-MOE_INLINE void ring_dots(const Ring<Q>& R, int s, int ng, const uint32_t (&wv)[16],
-                          float (&acc)[kMaxTokGroup][4]) {
+template <int Q, int NT, int JW>
+MOE_INLINE void ring_dots(const Ring<Q, NT>& R, int s, int ng, const uint32_t (&wv)[16],
+                          float (&acc)[NT][4]) {
 #pragma unroll
-  for (int t = 0; t < kMaxTokGroup; ++t)
+  for (int t = 0; t < NT; ++t)
     if (t < ng) dot16_bcast<JW>(acc[t], wv, R.xbuf[s][t]);
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -1255,28 +1256,28 @@ MOE_INLINE void ring_dots(const Ring<Q>& R, int s, int ng, const uint32_t (&wv)[
 // The four words of ring slot s.  For q <= 4 the lookups of word j + 1 are issued before the
 // products of word j, so the LDS latency is exposed once per chunk instead of once per word
 // (q >= 5 merges each looked-up pair with VALU work of its own and keeps the plain order).
-template <int Q>
-MOE_INLINE void ring_chunk(const Ring<Q>& R, int s, int ng, uint32_t lane4,
-                           float (&acc)[kMaxTokGroup][4]) {
+template <int Q, int NT>
+MOE_INLINE void ring_chunk(const Ring<Q, NT>& R, int s, int ng, uint32_t lane4,
+                           float (&acc)[NT][4]) {
   uint32_t wa[16], wb[16];
   if constexpr (Q <= 4) {
-    ring_decode<Q, 0>(R, s, lane4, wa);
-    ring_decode<Q, 1>(R, s, lane4, wb);
-    ring_dots<Q, 0>(R, s, ng, wa, acc);
-    ring_decode<Q, 2>(R, s, lane4, wa);
-    ring_dots<Q, 1>(R, s, ng, wb, acc);
-    ring_decode<Q, 3>(R, s, lane4, wb);
-    ring_dots<Q, 2>(R, s, ng, wa, acc);
-    ring_dots<Q, 3>(R, s, ng, wb, acc);
+    ring_decode<Q, NT, 0>(R, s, lane4, wa);
+    ring_decode<Q, NT, 1>(R, s, lane4, wb);
+    ring_dots<Q, NT, 0>(R, s, ng, wa, acc);
+    ring_decode<Q, NT, 2>(R, s, lane4, wa);
+    ring_dots<Q, NT, 1>(R, s, ng, wb, acc);
+    ring_decode<Q, NT, 3>(R, s, lane4, wb);
+    ring_dots<Q, NT, 2>(R, s, ng, wa, acc);
+    ring_dots<Q, NT, 3>(R, s, ng, wb, acc);
   } else {
-    ring_decode<Q, 0>(R, s, lane4, wa);
-    ring_dots<Q, 0>(R, s, ng, wa, acc);
-    ring_decode<Q, 1>(R, s, lane4, wa);
-    ring_dots<Q, 1>(R, s, ng, wa, acc);
-    ring_decode<Q, 2>(R, s, lane4, wa);
-    ring_dots<Q, 2>(R, s, ng, wa, acc);
-    ring_decode<Q, 3>(R, s, lane4, wa);
-    ring_dots<Q, 3>(R, s, ng, wa, acc);
+    ring_decode<Q, NT, 0>(R, s, lane4, wa);
+    ring_dots<Q, NT, 0>(R, s, ng, wa, acc);
+    ring_decode<Q, NT, 1>(R, s, lane4, wa);
+    ring_dots<Q, NT, 1>(R, s, ng, wa, acc);
+    ring_decode<Q, NT, 2>(R, s, lane4, wa);
+    ring_dots<Q, NT, 2>(R, s, ng, wa, acc);
+    ring_decode<Q, NT, 3>(R, s, lane4, wa);
+    ring_dots<Q, NT, 3>(R, s, ng, wa, acc);
   }
 }
 
@@ -1293,16 +1294,17 @@ MOE_INLINE void report_invalid(const KArgs& A, const Item& it, int mode) {
   }
 }
 
-// Process item `it` (index i) and every following item of the same width that is streamable.
-// On return, (i, it, ok) describe the first item not processed (i >= total: none left).
-template <int MODE, int Q>
+// Process item `it` (index i) and every following item of the same width that is streamable
+// with at most NT tokens.  On return, (i, it, ok) describe the first item not processed
+// (i >= total: none left).
+template <int MODE, int Q, int NT>
 MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& ok, int total,
                             int sh_tiles, int tiles) {
-  constexpr int D = Ring<Q>::D;
+  constexpr int D = Ring<Q, NT>::D;
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const uint32_t lane4 = static_cast<uint32_t>(lane) * 4u;
-  Ring<Q> R;
+  Ring<Q, NT> R;
   Geo cur, nxt;
   u32x4 L[kLutRegs];
   prefetch_lut_q<Q>(it, lane, wave, L);
@@ -1331,11 +1333,11 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
       next.expert = -1;
       next_ok = in_range && fill_item<MODE>(A, f, loc, next);
     }
-    cont = next_ok && next.q == Q && streamable<MODE>(A, next);
+    cont = next_ok && next.q == Q && streamable<MODE>(A, next) && next.n <= NT;
     if (cont) make_geo<MODE>(A, next, nxt);
     __syncthreads();
     if (cont) prefetch_lut_q<Q>(next, lane, wave, L);
-    float acc[kMaxTokGroup][4] = {};
+    float acc[NT][4] = {};
     // the wavefront walks its chunks padded to a multiple of D, so the next item's chunk k
     // always lands in slot k % D
     const int m = (cur.n + D - 1) / D * D;
@@ -1343,22 +1345,37 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
 #pragma unroll
       for (int s = 0; s < D; ++s) {
         const int v = v0 + s;
-        if (v < cur.n) ring_chunk<Q>(R, s, cur.ng, lane4, acc);
+        if (v < cur.n) ring_chunk<Q, NT>(R, s, cur.ng, lane4, acc);
         Geo g;
         int k;
         pick_refill(cur, nxt, cont, v + D, m, g, k);
         R.issue(s, g, k);
       }
     }
-    float tot[kMaxTokGroup];
+    float tot[NT];
 #pragma unroll
-    for (int t = 0; t < kMaxTokGroup; ++t) tot[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
-    reduce_and_store<MODE, kMaxTokGroup>(A, it, 0, it.n, tot, Qu);
+    for (int t = 0; t < NT; ++t) tot[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
+    reduce_and_store<MODE, NT>(A, it, 0, it.n, tot, Qu);
     i = queue_advance(Qu);
     it = next;
     ok = next_ok;
     if (!cont) return;
     cur = nxt;
+  }
+}
+
+template <int MODE, int NT>
+MOE_INLINE void stream_q(const KArgs& A, Queue& Qu, int& i, Item& it, bool& ok, int total, int sh_tiles,
+                         int tiles) {
+  switch (it.q) {
+    case 1: valu_stream<MODE, 1, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+    case 2: valu_stream<MODE, 2, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+    case 3: valu_stream<MODE, 3, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+    case 4: valu_stream<MODE, 4, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+    case 5: valu_stream<MODE, 5, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+    case 6: valu_stream<MODE, 6, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+    case 7: valu_stream<MODE, 7, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
+    default: valu_stream<MODE, 8, NT>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
   }
 }
 
@@ -1393,16 +1410,10 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
       continue;
     }
     if (streamable<MODE>(A, it)) {
-      switch (it.q) {
-        case 1: valu_stream<MODE, 1>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-        case 2: valu_stream<MODE, 2>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-        case 3: valu_stream<MODE, 3>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-        case 4: valu_stream<MODE, 4>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-        case 5: valu_stream<MODE, 5>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-        case 6: valu_stream<MODE, 6>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-        case 7: valu_stream<MODE, 7>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-        default: valu_stream<MODE, 8>(A, Qu, i, it, ok, total, sh_tiles, tiles); break;
-      }
+      // the ring loads as many activation rows as the item has tokens (1, 2, else 4)
+      if (it.n <= 1) stream_q<MODE, 1>(A, Qu, i, it, ok, total, sh_tiles, tiles);
+      else if (it.n == 2) stream_q<MODE, 2>(A, Qu, i, it, ok, total, sh_tiles, tiles);
+      else stream_q<MODE, 4>(A, Qu, i, it, ok, total, sh_tiles, tiles);
     } else {
       switch (it.q) {
         case 1: run_item<MODE, 1>(A, it, Qu); break;

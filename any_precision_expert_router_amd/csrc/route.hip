@@ -116,7 +116,7 @@ constexpr int kGroupMapBytes = 16384;  // LDS of the stable placement (slot map 
 
 struct GroupSmem {
   int32_t count[MOE_MAX_EXPERTS];
-  int32_t wave_tot[2][kGroupThreads / 64];
+  int32_t wave_tot[4][kGroupThreads / 64];
   union {
     uint8_t slot_map[kGroupMapBytes];     // small batches: token x expert slot map per chunk
     int32_t seg_pos[kGroupMapBytes / 4];  // large batches: [segments][E] pair counts, then positions
@@ -293,26 +293,46 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
     streaming = n <= kRecTok && n < r.dense_threshold;
     groups = !streaming && split && n > kRecGroupTok ? (n + kRecGroupTok - 1) / kRecGroupTok : 1;
   }
-  // exclusive scans of (records of multi-token experts) and (streaming experts)
-  const int a0 = tid < n_act && !streaming ? groups : 0, b0 = tid < n_act && streaming ? 1 : 0;
-  int a = a0, b = b0;
+  // exclusive scans of the records of multi-token experts, then of the streaming experts in three
+  // classes by token count (3-4, 2, 1): a streaming workgroup keeps its ring across consecutive
+  // items whose token count fits the ring's, so equal counts are kept together
+  const bool act_ = tid < n_act;
+  int v[4] = {act_ && !streaming ? groups : 0, act_ && streaming && n >= 3 ? 1 : 0,
+              act_ && streaming && n == 2 ? 1 : 0, act_ && streaming && n == 1 ? 1 : 0};
+  const int v0[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int a2 = __shfl_up(a, off, 64), b2 = __shfl_up(b, off, 64);
-    if (lane >= off) { a += a2; b += b2; }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int o = __shfl_up(v[c], off, 64);
+      if (lane >= off) v[c] += o;
+    }
   }
   __syncthreads();  // the grouping's last reads of wave_tot are done
-  if (lane == 63) { sm.wave_tot[0][wave] = a; sm.wave_tot[1][wave] = b; }
-  __syncthreads();
-  int base_a = 0, base_b = 0, tot_a = 0, tot_b = 0;
-  for (int w = 0; w < static_cast<int>(blockDim.x) / 64; ++w) {
-    const int ta = sm.wave_tot[0][w], tb = sm.wave_tot[1][w];
-    if (w < wave) { base_a += ta; base_b += tb; }
-    tot_a += ta;
-    tot_b += tb;
+  if (lane == 63) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sm.wave_tot[c][wave] = v[c];
   }
+  __syncthreads();
+  int cbase[4] = {0, 0, 0, 0}, tot[4] = {0, 0, 0, 0};
+  for (int w = 0; w < static_cast<int>(blockDim.x) / 64; ++w) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int t = sm.wave_tot[c][w];
+      if (w < wave) cbase[c] += t;
+      tot[c] += t;
+    }
+  }
+  int cls = 0;
+#pragma unroll
+  for (int c = 1; c < 4; ++c)
+    if (v0[c]) cls = c;
+  int first = 0;  // records of the classes before this expert's
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (c < cls) first += tot[c];
   if (tid < n_act) {
-    const int pos = streaming ? tot_a + base_b + b - b0 : base_a + a - a0;
+    const int pos = first + cbase[cls] + v[cls] - v0[cls];
     ExpertRecord rec;
     fill_record(rec, r.table[2 * e], r.table[2 * e + 1], r.I, r);
     rec.expert = e;
@@ -330,7 +350,7 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
     }
   }
   if (tid == 0) {
-    r.n_recs[0] = tot_a + tot_b;
+    r.n_recs[0] = tot[0] + tot[1] + tot[2] + tot[3];
     ExpertRecord rec{};
     if (r.shared) {
       fill_record(rec, r.shared[0], r.shared[1], r.I_shared, r);
