@@ -6,6 +6,7 @@ the single-block GEMV within 1e-5 relative L2 (fp32 accumulation of exact fp16 p
 layer outputs within 1e-3 relative L2 (fp32 accumulation, the SiLU-gated activation rounded
 once to fp16, y rounded to fp16: about 4e-4 expected).
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -661,4 +662,39 @@ def test_lynx_remapped_layer_matches_oracle():
                                                   oracle.committed_index(di, dq), dlut, x64[t:t + 1])[0]
     err = oracle.rel_l2(y.float().cpu().numpy().astype(np.float64), ref)
     say(f"  LYNX-remapped layer rel L2 {err:.2e}")
+    assert err <= LAYER_TOL
+
+
+@pytest.mark.parametrize("threshold", [0, 3], ids=["auto", "mfma-from-3"])
+def test_streaming_token_counts_and_ring_switches(threshold):
+    """Routing built so that experts 0-3 get 1 token, 4-7 get 2, 8-11 get 3 and 12-15 get 4 (top-2
+    over 20 tokens), at every width 1..8: the streaming ring loads 1, 2 or 4 activation rows by
+    token count, the record step orders the streaming experts by count, and a stream ends where
+    the next item's count does not fit its ring.  With the matrix-core switch at 3 tokens the 3-
+    and 4-token experts take the MFMA branch instead.  Output against the oracle."""
+    E, k = 16, 2
+    mult = [1] * 4 + [2] * 4 + [3] * 4 + [4] * 4
+    slots = [e for e in range(E) for _ in range(mult[e])]          # 40 (token, slot) pairs
+    T = len(slots) // k
+    # deal the pairs to tokens so that each token's two experts differ: token t takes slots t
+    # and t + T of the expert list (the list is sorted, so the two halves never coincide)
+    r = np.random.default_rng(7)
+    logits = (r.standard_normal((T, E)) * 0.1).astype(np.float32)
+    for t in range(T):
+        a, b = slots[t], slots[t + T]
+        assert a != b
+        logits[t, a] = 5.0
+        logits[t, b] = 4.0
+    ids, _ = oracle.route_topk(logits, k)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    np.testing.assert_array_equal(counts, mult)
+    shape = wl.TINY.replace(H=256, E=E, I=384, k=k, T=T, name="token-count rings")
+    q = np.array([[1 + (e + 3 * m) % 8 for m in range(2)] for e in range(E)], dtype=np.uint8)
+    inputs = dataclasses.replace(wl.gen_layer_inputs(shape), logits=logits)
+    dl = gpu_layers.device_layer(shape, q_override=q)
+    y, _ = _run_layer(shape, inputs, dl, threshold=threshold)
+    get, _ = gpu_layers.oracle_getters(shape, q)
+    ref = oracle.layer_forward(inputs.x, logits, k, get)
+    err = oracle.rel_l2(y, ref["y"])
+    say(f"  token-count rings (threshold {threshold}): rel L2 {err:.2e}")
     assert err <= LAYER_TOL
