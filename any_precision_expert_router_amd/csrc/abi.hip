@@ -104,7 +104,7 @@ Workspace carve_workspace(void* base, int T, int E, int H, int I, int k, int I_s
   const size_t o_act = take(TK * I * sizeof(uint16_t));
   const size_t o_act_sh = take(static_cast<size_t>(T) * I_shared * sizeof(uint16_t));
   w.segs = down_segments(I, static_cast<int>(TK));
-  w.segs_shared = I_shared > 0 ? down_segments(I_shared, T) : 1;
+  w.segs_shared = I_shared > 0 ? down_segments(I_shared, T, kSegChunksShared) : 1;
   const size_t o_part = take(w.segs * TK * H * sizeof(float));
   const size_t o_part_sh =
       take(I_shared > 0 ? w.segs_shared * static_cast<size_t>(T) * H * sizeof(float) : 0);

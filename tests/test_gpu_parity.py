@@ -258,8 +258,8 @@ def test_layer_with_shared_expert_and_scale(threshold):
 @pytest.mark.parametrize("threshold", [0, 1, 1000], ids=["auto", "all-mfma", "valu-max"])
 def test_layer_long_down_rows_split_into_segments(threshold):
     """Down rows long enough to be cut into column segments (routed: 26 chunks of 128 columns ->
-    2 segments of 13; shared: 41 chunks -> 3 segments of 13/14/14, every wavefront share ragged),
-    each with its own partial sums, summed by the combine."""
+    2 segments of 13; shared: 41 chunks -> 4 segments of 10/10/10/11, every wavefront share
+    ragged), each with its own partial sums, summed by the combine."""
     shape = wl.TINY.replace(H=128, E=6, I=26 * 128, k=2, T=7, I_shared=41 * 128, q_shared=8,
                             name="segmented down rows")
     q = np.array([[3 + (e + m) % 6 for m in range(2)] for e in range(shape.E)], dtype=np.uint8)
