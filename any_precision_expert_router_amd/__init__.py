@@ -31,7 +31,8 @@ EXPORTED = (
     "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
     "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_hbm_read_probe",
     "moe_routing_stats", "moe_workspace_routing", "moe_commit_blocks", "moe_plan_widths",
-    "moe_substitute", "moe_lynx_remap",
+    "moe_substitute", "moe_lynx_remap", "moe_page_reload", "moe_page_commit",
+    "moe_page_offload",
     "moe_last_error",
 )
 
@@ -82,7 +83,10 @@ def _load():
         "moe_hbm_read_probe": ([P, Z, P, S], I),
         "moe_routing_stats": ([P, P, P, I, I, I, P, P, P, P, S], I),
         "moe_workspace_routing": ([P, Z, I, I, I, I, I, I, P, P, P, P], I),
-        "moe_commit_blocks": ([P, P, P, I, S], I),
+        "moe_commit_blocks": ([P, I, P, P, I, S], I),
+        "moe_page_reload": ([P, I, I, P, P, P, P, P, S, S], I),
+        "moe_page_commit": ([P, I, I, P, P, S], I),
+        "moe_page_offload": ([P, I, I, P, P, P, P, P, S, S], I),
         "moe_substitute": ([P, I, I, I, P, I, ctypes.c_float, P, P, P, P, P, ctypes.c_float, P, S], I),
         "moe_lynx_remap": ([P, I, I, I, ctypes.c_float, P, P, P, S], I),
         "moe_plan_widths": ([I, P, P, P, P, P, P, ctypes.c_int64, P, P], I),
@@ -247,15 +251,29 @@ def moe_substitute(logits, resident, policy, topk_ids, topk_gates, missed, fetch
 def moe_lynx_remap(logits, topk_ids, remapped, critical, bin_width=None, stream=None) -> None:
     """Remap low-confidence slots of topk_ids (device int32 [T,k], in place) onto the critical
     expert set; remapped gets each remapped slot's original expert (else -1), critical [E] the
-    set.  bin_width defaults to k/E in fp32.  See the header for the readings."""
+    set.  bin_width None lets the library take its default, k/E in fp32.  See the header for
+    the readings."""
     T, E = logits.shape
     k = topk_ids.shape[1] if topk_ids.dim() == 2 else topk_ids.numel() // max(T, 1)
     if bin_width is None:
-        import numpy as _np
-        bin_width = float(_np.float32(k) / _np.float32(E))
+        bin_width = 0.0
     _check("moe_lynx_remap", _lib.moe_lynx_remap(
         _ptr(logits), T, E, k, float(bin_width), _ptr(topk_ids), _ptr(remapped), _ptr(critical),
         _stream(stream)))
+
+
+def _event(ev, stream) -> int:
+    """Raw hipEvent_t of a torch.cuda.Event (torch creates the event at its first record, so an
+    unrecorded one is recorded once on `stream` first) or an int handle."""
+    if isinstance(ev, int):
+        return ev
+    if not ev.cuda_event:
+        ev.record(stream)
+    return ev.cuda_event
+
+
+def _table_len(table) -> int:
+    return table.numel() * table.element_size() // ctypes.sizeof(ApqBlock)
 
 
 def moe_commit_blocks(table, index, descs, stream=None) -> None:
@@ -264,7 +282,36 @@ def moe_commit_blocks(table, index, descs, stream=None) -> None:
     n = len(index)
     idx = (ctypes.c_int32 * max(n, 1))(*[int(i) for i in index])
     arr = (ApqBlock * max(n, 1))(*descs)
-    _check("moe_commit_blocks", _lib.moe_commit_blocks(_ptr(table), idx, arr, n, _stream(stream)))
+    _check("moe_commit_blocks", _lib.moe_commit_blocks(_ptr(table), _table_len(table), idx, arr, n,
+                                                       _stream(stream)))
+
+
+def moe_page_reload(table, index: int, current: ApqBlock, target: ApqBlock, host_planes, host_lut,
+                    copy_event, copy_stream, stream=None) -> None:
+    """Copy a block's missing planes and its LUT from pinned host tensors on copy_stream and
+    record copy_event there; a block coming back from the host is marked in transfer on `stream`
+    first.  `target` is committed later by moe_page_commit (see the header for the rules)."""
+    _check("moe_page_reload", _lib.moe_page_reload(
+        _ptr(table), _table_len(table), int(index), ctypes.byref(current), ctypes.byref(target),
+        _ptr(host_planes), _ptr(host_lut), _event(copy_event, copy_stream), _stream(copy_stream),
+        _stream(stream)))
+
+
+def moe_page_commit(table, index: int, target: ApqBlock, copy_event, stream=None) -> None:
+    """The safe boundary of a reload: `stream` waits for copy_event, then `target` is committed."""
+    _check("moe_page_commit", _lib.moe_page_commit(
+        _ptr(table), _table_len(table), int(index), ctypes.byref(target), _event(copy_event, stream),
+        _stream(stream)))
+
+
+def moe_page_offload(table, index: int, current: ApqBlock, target: ApqBlock, host_planes, host_lut,
+                     copy_event, copy_stream, stream=None) -> None:
+    """Commit `target` (evicted to the host, or a lower width) on `stream`, then copy the planes
+    (and LUT) that leave the device into pinned host tensors on copy_stream (None: no copy)."""
+    _check("moe_page_offload", _lib.moe_page_offload(
+        _ptr(table), _table_len(table), int(index), ctypes.byref(current), ctypes.byref(target),
+        _ptr(host_planes), _ptr(host_lut), _event(copy_event, copy_stream), _stream(copy_stream),
+        _stream(stream)))
 
 
 def moe_plan_widths(q_cur, q_floor, rows, cols, damage, mult, target_bytes):

@@ -163,6 +163,25 @@ int check_block_host(const moe_apq_block* b) {
   return MOE_OK;
 }
 
+// The FFN kernels address activation rows (x [T][H], act [T*k][I], act_shared [T][I_shared], a
+// plain block's x [T][cols]) through buffer resources whose size and offsets are 32-bit byte
+// counts, so every such array must stay below 4 GiB.
+int check_act_range(const char* what, size_t rows, size_t cols) {
+  const size_t bytes = rows * cols * sizeof(uint16_t);
+  if (bytes >= (static_cast<size_t>(1) << 32))
+    return set_error(MOE_EUNSUPPORTED, "%s of %zu x %zu fp16 values is %zu bytes: activation arrays "
+                     "must stay below 4 GiB", what, rows, cols, bytes);
+  return MOE_OK;
+}
+
+int check_ffn_range(int T, int H, int I, int k, int I_shared) {
+  if (int rc = check_act_range("x", static_cast<size_t>(T), static_cast<size_t>(H))) return rc;
+  if (int rc = check_act_range("act", static_cast<size_t>(T) * k, static_cast<size_t>(I))) return rc;
+  if (I_shared > 0)
+    if (int rc = check_act_range("act_shared", static_cast<size_t>(T), static_cast<size_t>(I_shared))) return rc;
+  return MOE_OK;
+}
+
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -215,6 +234,7 @@ int moe_apq_ffn(const moe_apq_block* table, int E, int H, int I, const uint16_t*
       !topk_gates || !y)
     return set_error(MOE_EINVAL, "NULL pointer argument");
   const int ish = shared ? I_shared : 0;
+  if (int rc = check_ffn_range(T, H, I, k, ish)) return rc;
   const Workspace ws = carve_workspace(workspace, T, E, H, I, k, ish);
   if (!workspace || ws_bytes < ws.bytes)
     return set_error(MOE_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
@@ -238,6 +258,7 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int T, int E, int 
   if (T == 0) return MOE_OK;
   if (!logits || !x || !table || !y) return set_error(MOE_EINVAL, "NULL pointer argument");
   const int ish = shared ? I_shared : 0;
+  if (int rc = check_ffn_range(T, H, I, k, ish)) return rc;
   const Workspace ws = carve_workspace(workspace, T, E, H, I, k, ish);
   if (!workspace || ws_bytes < ws.bytes)
     return set_error(MOE_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
@@ -266,6 +287,7 @@ int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float*
   if (T < 0 || T > MOE_MAX_TOKENS) return set_error(MOE_EUNSUPPORTED, "T=%d outside 0..%d", T, MOE_MAX_TOKENS);
   if (T == 0) return MOE_OK;
   if (!x || !y) return set_error(MOE_EINVAL, "NULL pointer argument");
+  if (int rc = check_act_range("x", static_cast<size_t>(T), static_cast<size_t>(blk_host->cols))) return rc;
   moe_apq_block b = *blk_host;
   b.state = MOE_PAGE_GPU;
   return launch_apq_gemv(b, x, T, y, dense_threshold, as_stream(stream));
@@ -329,27 +351,57 @@ int moe_lynx_remap(const float* logits, int T, int E, int k, float bin_width, in
                    int32_t* remapped, uint8_t* critical, void* stream) {
   clear_error();
   if (int rc = check_route_args(T, E, k)) return rc;
-  if (!(bin_width > 0.0f) || !(bin_width <= FLT_MAX))
-    return set_error(MOE_EINVAL, "bin_width must be positive and finite");
+  if (!(bin_width <= FLT_MAX))
+    return set_error(MOE_EINVAL, "bin_width must be finite (<= 0 selects k/E)");
+  // AffinityBinning's bins follow from the sparsity ratio k/N alone: the default width is k/E,
+  // one fp32 division
+  if (bin_width <= 0.0f) bin_width = static_cast<float>(k) / static_cast<float>(E);
   if (!critical) return set_error(MOE_EINVAL, "NULL pointer argument");
   if (T > 0 && (!logits || !topk_ids || !remapped)) return set_error(MOE_EINVAL, "NULL pointer argument");
   return launch_lynx_remap(logits, T, E, k, bin_width, topk_ids, remapped, critical, as_stream(stream));
 }
 
-int moe_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
-                      void* stream) {
+int moe_commit_blocks(moe_apq_block* table, int table_len, const int32_t* index,
+                      const moe_apq_block* desc, int n, void* stream) {
   clear_error();
   if (n < 0) return set_error(MOE_EINVAL, "n=%d < 0", n);
+  if (table_len <= 0) return set_error(MOE_EINVAL, "table_len=%d must be positive", table_len);
   if (n == 0) return MOE_OK;
   if (!table || !index || !desc) return set_error(MOE_EINVAL, "NULL pointer argument");
+  std::vector<uint8_t> seen(static_cast<size_t>(table_len), 0);
   for (int i = 0; i < n; ++i) {
-    if (index[i] < 0) return set_error(MOE_EINVAL, "index[%d]=%d < 0", i, index[i]);
+    if (index[i] < 0 || index[i] >= table_len)
+      return set_error(MOE_EINVAL, "index[%d]=%d outside the table [0, %d)", i, index[i], table_len);
+    if (seen[index[i]]++)
+      return set_error(MOE_EINVAL, "index[%d]=%d repeats an earlier entry of the same commit", i, index[i]);
     const moe_apq_block& b = desc[i];
     if (b.q < 1 || b.q > 8) return set_error(MOE_EINVAL, "desc[%d]: q=%d outside 1..8", i, b.q);
     if (b.rows <= 0 || b.cols <= 0 || b.rows % kRowPanel || b.cols % kColChunk)
       return set_error(MOE_EINVAL, "desc[%d]: need rows %% 64 == 0 and cols %% 128 == 0", i);
   }
   return launch_commit_blocks(table, index, desc, n, as_stream(stream));
+}
+
+int moe_page_reload(moe_apq_block* table, int table_len, int index, const moe_apq_block* current,
+                    const moe_apq_block* target, const void* host_planes, const void* host_lut,
+                    void* copy_event, void* copy_stream, void* stream) {
+  clear_error();
+  return page_reload(table, table_len, index, current, target, host_planes, host_lut,
+                     static_cast<hipEvent_t>(copy_event), as_stream(copy_stream), as_stream(stream));
+}
+
+int moe_page_commit(moe_apq_block* table, int table_len, int index, const moe_apq_block* target,
+                    void* copy_event, void* stream) {
+  clear_error();
+  return page_commit(table, table_len, index, target, static_cast<hipEvent_t>(copy_event), as_stream(stream));
+}
+
+int moe_page_offload(moe_apq_block* table, int table_len, int index, const moe_apq_block* current,
+                     const moe_apq_block* target, void* host_planes, void* host_lut, void* copy_event,
+                     void* copy_stream, void* stream) {
+  clear_error();
+  return page_offload(table, table_len, index, current, target, host_planes, host_lut,
+                      static_cast<hipEvent_t>(copy_event), as_stream(copy_stream), as_stream(stream));
 }
 
 int moe_workspace_routing(void* workspace, size_t ws_bytes, int T, int E, int H, int I, int k,

@@ -1294,6 +1294,22 @@ MOE_INLINE void report_invalid(const KArgs& A, const Item& it, int mode) {
   }
 }
 
+// A skipped down item (its record names an invalid block) still owns its rows of the partial
+// sums: they are written as zeros, so that the combine adds nothing for the skipped expert and
+// y stays defined for its tokens.
+template <int MODE>
+MOE_INLINE void zero_skipped_rows(const KArgs& A, const Item& it) {
+  if constexpr (MODE == kDown) {
+    for (int i = static_cast<int>(threadIdx.x); i < it.n * kRowPanel; i += kThreads) {
+      const int t = i / kRowPanel, l = i - t * kRowPanel;
+      float* dst = it.shared
+                       ? A.part_shared + (static_cast<size_t>(it.seg) * A.T + t) * A.H
+                       : A.part + (static_cast<size_t>(it.seg) * A.T * A.k + A.pairs[it.src_base + t]) * A.H;
+      dst[it.r0 + l] = 0.0f;
+    }
+  }
+}
+
 // Process item `it` (index i) and every following item of the same width that is streamable
 // with at most NT tokens.  On return, (i, it, ok) describe the first item not processed
 // (i >= total: none left).
@@ -1403,6 +1419,7 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
   while (i < total) {
     if (!ok) {  // skip an item whose page-table descriptor is invalid
       report_invalid(A, it, MODE);
+      zero_skipped_rows<MODE>(A, it);
       queue_publish(Qu);
       __syncthreads();
       i = queue_advance(Qu);

@@ -181,6 +181,14 @@ int launch_routing_stats(const int32_t* offsets, const int32_t* pairs, const flo
                          double* sums, hipStream_t stream);
 int launch_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
                          hipStream_t stream);
+int page_reload(moe_apq_block* table, int table_len, int index, const moe_apq_block* cur,
+                const moe_apq_block* tgt, const void* host_planes, const void* host_lut,
+                hipEvent_t copy_event, hipStream_t copy_stream, hipStream_t stream);
+int page_commit(moe_apq_block* table, int table_len, int index, const moe_apq_block* tgt,
+                hipEvent_t copy_event, hipStream_t stream);
+int page_offload(moe_apq_block* table, int table_len, int index, const moe_apq_block* cur,
+                 const moe_apq_block* tgt, void* host_planes, void* host_lut, hipEvent_t copy_event,
+                 hipStream_t copy_stream, hipStream_t stream);
 int launch_substitute(const float* logits, int T, int E, int k, const uint8_t* resident, int policy,
                       float gate_threshold, int32_t* ids, const float* gates, int32_t* missed,
                       uint8_t* fetch, float* admit_mass, float admit_threshold, uint8_t* admit,

@@ -11,9 +11,12 @@
 // Grouping (LYNX, 1 Problem statement: decode loads each distinct expert the batch activates):
 // one workgroup.  Counts per expert by LDS integer atomics (order-free, so deterministic), an
 // exclusive scan for the CSR offsets and the ascending active-expert list, then a stable
-// placement: because the k experts of one token are distinct, a pair's rank inside its expert
-// is the number of earlier tokens that picked that expert.  Tokens are walked in chunks through
-// an LDS token x expert slot map, one thread per expert.
+// placement (pair id ascending inside an expert).  Routing output names k distinct experts per
+// token, so a pair's rank inside its expert is the number of earlier pairs that picked that
+// expert: small batches walk an LDS token x expert slot map with one thread per expert, large
+// batches run a segmented counting sort (one wavefront per run of tokens).  The standalone
+// grouping also accepts ids it did not produce: an id outside [0, E) is not placed, and a token
+// that names an expert twice is placed in slot order.
 #include "internal.hpp"
 
 namespace moeapq {
@@ -121,6 +124,7 @@ struct GroupSmem {
     uint8_t slot_map[kGroupMapBytes];     // small batches: token x expert slot map per chunk
     int32_t seg_pos[kGroupMapBytes / 4];  // large batches: [segments][E] pair counts, then positions
   };
+  int32_t dup_tag[kGroupMapBytes / 4];    // large batches: [segments][E] last token that named e
   int32_t offsets[MOE_MAX_EXPERTS + 1];  // LDS copies of the grouping results for the records
   int32_t active[MOE_MAX_EXPERTS];
   int32_t n_active;
@@ -140,7 +144,11 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
 
   for (int e = tid; e < E; e += kGroupThreads) sm.count[e] = 0;
   __syncthreads();
-  for (int p = tid; p < TK; p += kGroupThreads) atomicAdd(&sm.count[ids[p]], 1);
+  // an id outside [0, E) names no expert: its pair is not placed (offsets[E] counts placed pairs)
+  for (int p = tid; p < TK; p += kGroupThreads) {
+    const int e = ids[p];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&sm.count[e], 1);
+  }
   __syncthreads();
 
   // exclusive scans of count[e] and of (count[e] > 0), one thread per expert (E <= 1024)
@@ -182,15 +190,23 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
     // stable placement by a segmented counting sort: the tokens are cut into S consecutive
     // segments, one per wavefront; each wavefront counts its segment's pairs per expert, a
     // per-expert prefix over the segments (starting at the expert's offset) gives each segment its
-    // first position, and each wavefront then walks its tokens in order.  Because the k experts
-    // of one token are distinct, the k lanes of a token never update the same position counter.
+    // first position, and each wavefront then walks its tokens in order, lane j placing slot j.
+    // When a token's k experts are distinct (always so for routing output), its k lanes never
+    // update the same position counter; a token that names an expert twice takes an exact,
+    // slower path that keeps the slot order.
     const int S = max(1, min(kGroupThreads / 64, static_cast<int>(kGroupMapBytes / (4 * E))));
     const int seg_len = (T + S - 1) / S;
-    for (int i = tid; i < S * E; i += kGroupThreads) sm.seg_pos[i] = 0;
+    for (int i = tid; i < S * E; i += kGroupThreads) {
+      sm.seg_pos[i] = 0;
+      sm.dup_tag[i] = -1;
+    }
     __syncthreads();
     const int t_begin = min(T, wave * seg_len), t_end = min(T, t_begin + seg_len);
     if (wave < S) {
-      for (int i = t_begin * k + lane; i < t_end * k; i += 64) atomicAdd(&sm.seg_pos[wave * E + ids[i]], 1);
+      for (int i = t_begin * k + lane; i < t_end * k; i += 64) {
+        const int e = ids[i];
+        if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&sm.seg_pos[wave * E + e], 1);
+      }
     }
     __syncthreads();
     if (tid < E) {
@@ -204,18 +220,60 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
     __syncthreads();
     if (wave < S && lane < k) {
       constexpr int kBatch = 16;  // expert ids loaded ahead of the in-order placement
+      int32_t* pos_of = sm.seg_pos + wave * E;
+      int32_t* tag_of = sm.dup_tag + wave * E;
       for (int t0 = t_begin; t0 < t_end; t0 += kBatch) {
         int e[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) e[u] = t0 + u < t_end ? ids[(t0 + u) * k + lane] : 0;
+        for (int u = 0; u < kBatch; ++u) e[u] = t0 + u < t_end ? ids[(t0 + u) * k + lane] : -1;
+        // Two slots of one token naming the same expert: each valid slot swaps its token into
+        // the expert's tag; the later of two such slots gets its own token back.  The swaps of
+        // a token complete before the next token's (one LDS instruction each, in order).
+        bool clash[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const bool valid = static_cast<unsigned>(e[u]) < static_cast<unsigned>(E);
+          clash[u] = valid && atomicExch(&tag_of[valid ? e[u] : 0], t0 + u) == t0 + u;
+        }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           if (t0 + u < t_end) {
             const int p = (t0 + u) * k + lane;
-            const int pos = sm.seg_pos[wave * E + e[u]];
-            sm.seg_pos[wave * E + e[u]] = pos + 1;
-            if (pairs_lds) pairs_lds[pos] = p;
-            pairs[pos] = p;
+            const int eu = e[u];
+            const bool valid = static_cast<unsigned>(eu) < static_cast<unsigned>(E);
+            if (__ballot(clash[u]) == 0) {
+              // distinct experts: the token's slots never share a position counter
+              if (valid) {
+                const int pos = pos_of[eu];
+                pos_of[eu] = pos + 1;
+                if (pairs_lds) pairs_lds[pos] = p;
+                pairs[pos] = p;
+              }
+            } else {
+              // repeated experts: the first slot naming an expert takes positions for all of
+              // them, each slot its rank among them (slot order, so the sort stays stable)
+              int rank = 0, cnt = 0, first = lane;
+              for (int j2 = 0; j2 < k; ++j2) {
+                const int e2 = __shfl(eu, j2, 64);
+                if (e2 == eu) {
+                  if (j2 < lane) {
+                    ++rank;
+                    first = min(first, j2);
+                  }
+                  ++cnt;
+                }
+              }
+              int base = 0;
+              if (valid && rank == 0) {
+                base = pos_of[eu];
+                pos_of[eu] = base + cnt;
+              }
+              base = __shfl(base, first, 64);
+              if (valid) {
+                if (pairs_lds) pairs_lds[base + rank] = p;
+                pairs[base + rank] = p;
+              }
+            }
           }
         }
       }

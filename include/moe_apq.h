@@ -41,7 +41,9 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)       /* bad scalar argument (k > E, bad shape, q outside 1..8, NULL) */
-#define MOE_EUNSUPPORTED (-2) /* outside the instantiated bounds below                        */
+#define MOE_EUNSUPPORTED (-2) /* outside the instantiated bounds below, or an activation array
+                                 (x [T][H], act [T*k][I], act_shared [T][I_shared]) of 4 GiB or
+                                 more: the kernels address them with 32-bit byte offsets        */
 #define MOE_EWORKSPACE (-3)   /* workspace missing or smaller than moe_workspace_bytes()       */
 #define MOE_EHIP (-4)         /* a HIP launch or runtime call failed                           */
 #define MOE_EDEVICE (-5)      /* a kernel found an invalid block descriptor (see below)        */
@@ -111,8 +113,14 @@ int moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, 
 /*
  * Group the T*k (token, slot) pairs p = t*k + j by expert (LYNX 1: the set of distinct experts is
  * what a decode batch loads).  Stable counting sort.
- *   expert_offsets out int32 [E+1]: expert e's pairs are sorted_pairs[offsets[e] .. offsets[e+1]).
- *   sorted_pairs   out int32 [T*k]: pair ids, expert ascending, p ascending inside an expert.
+ *   topk_ids       int32 [T][k].  Routing output names k distinct experts in [0, E) per token;
+ *                  other ids are accepted with a defined result: a pair whose id is outside
+ *                  [0, E) names no expert and is not placed, and a token that names one expert
+ *                  in several slots has each of those pairs placed (in slot order).
+ *   expert_offsets out int32 [E+1]: expert e's pairs are sorted_pairs[offsets[e] .. offsets[e+1]);
+ *                  offsets[E] = number of placed pairs (T*k when every id is in [0, E)).
+ *   sorted_pairs   out int32 [T*k]: pair ids, expert ascending, p ascending inside an expert;
+ *                  entries from offsets[E] on are not written.
  *   active_experts out int32 [E]: experts with >= 1 pair, ascending, then -1 padding.
  *   n_active       out int32 [1].
  *   workspace/ws_bytes: unused (may be NULL/0); kept for ABI stability.
@@ -129,19 +137,24 @@ int moe_group_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t* e
  *   table        device moe_apq_block [E][2] (index e*2 + 0 = gate_up, e*2 + 1 = down).  Blocks
  *                may each have a different q.
  *   x            fp16 [T][H].
- *   expert_offsets, sorted_pairs, active_experts, n_active: from moe_group_by_expert.
+ *   expert_offsets, sorted_pairs, active_experts, n_active: from moe_group_by_expert, with
+ *                every pair placed (every id in [0, E)); a pair left out has no term in y.
  *   topk_gates   fp32 [T][k] from moe_route_topk.
  *   shared       device moe_apq_block [2] (gate_up [2*I_shared x H], down [H x I_shared]) or
  *                NULL (then I_shared is ignored); shared_scale fp32 [T] or NULL (= 1).
- *   prefill_threshold: tiles of experts with at least min(prefill_threshold, 5) routed pairs (and
- *                the shared expert's tiles when T reaches it) use the matrix-core (MFMA) product
- *                path, the others the packed-dot VALU path (<= 0: library default, 5).  Results
- *                agree up to fp32 summation order.
+ *   prefill_threshold: the token count n_e at or above which an expert's tiles (and the shared
+ *                expert's, with n = T) use the matrix-core (MFMA) product path instead of the
+ *                packed-dot VALU path; <= 0 selects the library default, 5.  The VALU path
+ *                holds at most 4 tokens per pass, so values above 5 act as 5: an expert with 5
+ *                or more tokens always takes the MFMA path.  Results agree up to fp32
+ *                summation order.
  *   y            out fp16 [T][H].
  *   workspace    >= moe_workspace_bytes(T, E, H, I, k, I_shared) bytes, 256-byte aligned.
  *   Device checks: a routed block whose descriptor does not match (rows, cols) of its module, has
  *   q outside 1..8 or is not MOE_PAGE_GPU is skipped and recorded in the workspace error word;
- *   moe_check_device_error() reports it.  Accuracy: fp32 accumulation, the SiLU-gated activation
+ *   moe_check_device_error() reports it.  The skipped expert contributes zero to y (its tokens
+ *   keep their other experts' terms), so y stays defined.  Host checks: MOE_EUNSUPPORTED when
+ *   T*H, T*k*I or T*I_shared fp16 values reach 4 GiB.  Accuracy: fp32 accumulation, the SiLU-gated activation
  *   rounded once to fp16, y rounded to fp16.
  */
 int moe_apq_ffn(const moe_apq_block* table, int E, int H, int I, const uint16_t* x, int T, int k,
@@ -289,9 +302,10 @@ int moe_substitute(const float* logits, int T, int E, int k, const uint8_t* resi
  * Device arguments: logits fp32 [T,E] (finite); topk_ids int32 [T,k] (in: routing output in
  * routing order; out: after remapping); remapped int32 [T,k] (out: the original expert of a
  * remapped slot, else -1); critical uint8 [E] (out: 1 = expert in the critical set).  bin_width
- * is a host scalar, normally (float)k / (float)E.  One workgroup; nothing is allocated.
- * Errors: MOE_EINVAL (bad T/E/k, bin_width not positive and finite, NULL), MOE_EUNSUPPORTED
- * (bounds), MOE_EHIP.
+ * is a host scalar; bin_width <= 0 selects the page's default, k/E computed as one fp32
+ * division (float)k / (float)E.  One workgroup; nothing is allocated.
+ * Errors: MOE_EINVAL (bad T/E/k, bin_width NaN or infinite, NULL), MOE_EUNSUPPORTED (bounds),
+ * MOE_EHIP.
  */
 int moe_lynx_remap(const float* logits, int T, int E, int k, float bin_width, int32_t* topk_ids,
                    int32_t* remapped, uint8_t* critical, void* stream);
@@ -306,13 +320,67 @@ int moe_lynx_remap(const float* logits, int T, int E, int k, float bin_width, in
  * planes of width q' are the first q' planes) and the LUT of width q'; raising it is a commit
  * after the missing planes and the new LUT have been copied in (e.g. an asynchronous copy from
  * pinned host memory on another stream, which `stream` waits for with an event).
- * table: device page table; index (host) [n]: entries to overwrite; desc (host) [n]: the new
- * descriptors, copied by value into the launch (both host arrays may be reused on return).
- * Nothing is allocated.  Errors: MOE_EINVAL (n < 0, NULL, negative index, q outside 1..8,
- * rows % 64 or cols % 128), MOE_EHIP.
+ * table: device page table of table_len entries (2*E for a layer's [E][2] table, 2 for a shared
+ * pair); index (host) [n]: entries to overwrite, each in [0, table_len) and none repeated;
+ * desc (host) [n]: the new descriptors, copied by value into the launch (both host arrays may
+ * be reused on return).  Nothing is allocated on the device.  Errors: MOE_EINVAL (n < 0,
+ * table_len <= 0, NULL, an index outside the table or repeated, q outside 1..8, rows % 64 or
+ * cols % 128), MOE_EHIP.  For page moves (offload to the host, reload from it) see
+ * moe_page_offload / moe_page_reload, which commit through this same stream-ordered write.
  */
-int moe_commit_blocks(moe_apq_block* table, const int32_t* index, const moe_apq_block* desc, int n,
-                      void* stream);
+int moe_commit_blocks(moe_apq_block* table, int table_len, const int32_t* index,
+                      const moe_apq_block* desc, int n, void* stream);
+
+/*
+ * Asynchronous page movement between device and host memory.
+ *
+ * Source: PagedWeight, Key Components 1 (a block's pages are GPU-resident, CPU-resident or in
+ * transfer) and Key Components 3 (offload and reload run asynchronously beside the computation;
+ * a changed bit width is committed only at a safe boundary).  Because the q-bit planes are a
+ * prefix of the wider ones, lowering a width drops trailing planes and raising it copies only
+ * the missing ones.
+ *
+ * Both calls take the page table (device, table_len entries) and the entry `index`, the entry's
+ * descriptor as committed now (`current`, host) and the one to commit (`target`, host), a
+ * caller-owned hipEvent_t `copy_event`, a side stream `copy_stream` for the copies and the
+ * compute `stream` on which the layer calls run.  Host buffers are pinned host memory
+ * (hipHostMalloc) holding the planes plane-major as moe_apq_pack writes them (plane p at byte
+ * p*rows*cols/8) and the LUT [rows][2^q] fp16; pageable memory makes the copies synchronous.
+ * Nothing is allocated.  Host-side state rules (checked before anything is issued, MOE_EINVAL):
+ *
+ * moe_page_reload: target->state is MOE_PAGE_GPU and target has the current shape.
+ *   current GPU-resident at width q' (raise the width): target names the same planes, q > q',
+ *     and a new LUT buffer; planes q'..q-1 and the LUT are copied; calls issued before the
+ *     final commit keep running at width q'.
+ *   current MOE_PAGE_CPU (bring back): the entry is committed as MOE_PAGE_IN_TRANSFER on
+ *     `stream` first (later calls skip the block and report MOE_EDEVICE), then all q planes and
+ *     the LUT are copied.
+ *   current MOE_PAGE_IN_TRANSFER: refused (a reload is already in flight).
+ *   Copies run on copy_stream, then copy_event is recorded there.  The call does not commit
+ *   target: layer calls issued on `stream` afterwards keep running at width q' (or skip the
+ *   block in transfer) while the copy proceeds beside them.
+ * moe_page_commit: the safe boundary of a reload.  `stream` waits for copy_event, then target
+ *   (the descriptor given to the moe_page_reload that recorded copy_event; state MOE_PAGE_GPU)
+ *   is committed: no call ever reads a width whose planes have not all landed, and every call
+ *   issued after it reads the new width.
+ * moe_page_offload: current must be MOE_PAGE_GPU.
+ *   target MOE_PAGE_CPU (evict): all planes and the LUT are copied to host_planes / host_lut
+ *     (each may be NULL when the host already holds them).
+ *   target MOE_PAGE_GPU with the same planes and 1 <= q < q' (lower the width; its LUT of width
+ *     q must be on the device already): planes q..q'-1 go to host_planes (may be NULL).
+ *   The commit of target is issued on `stream` first; the copies wait for every call issued
+ *   before it, so once copy_event has completed the host copies are whole and the device memory
+ *   that left may be reused.
+ * Errors: MOE_EINVAL (the rules above, NULL, index outside the table, bad shape or q), MOE_EHIP.
+ */
+int moe_page_reload(moe_apq_block* table, int table_len, int index, const moe_apq_block* current,
+                    const moe_apq_block* target, const void* host_planes, const void* host_lut,
+                    void* copy_event, void* copy_stream, void* stream);
+int moe_page_commit(moe_apq_block* table, int table_len, int index, const moe_apq_block* target,
+                    void* copy_event, void* stream);
+int moe_page_offload(moe_apq_block* table, int table_len, int index, const moe_apq_block* current,
+                     const moe_apq_block* target, void* host_planes, void* host_lut, void* copy_event,
+                     void* copy_stream, void* stream);
 
 /*
  * Greedy bit-width plan (host, synchronous; no device access).

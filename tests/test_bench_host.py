@@ -55,6 +55,17 @@ def test_headline_bytes_and_prefill_flops():
     assert 2.0 * p.T * p.k * 3 * p.H * p.I == 901943132160.0
 
 
+def test_default_workload_is_the_largest_mixed_width_decode_shape():
+    """The headline is the Qwen2-57B-A14B-shaped layer at 128 decode tokens with widths drawn from
+    {3, 4, 6, 8}; every other shape of the pages' models is a sub-record of the same line."""
+    shape = bench.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    assert (shape.H, shape.E, shape.I, shape.k, shape.T) == (3584, 64, 2560, 8, 128)
+    assert sorted(set(int(v) for v in np.unique(wl.gen_widths(shape)))) == [3, 4, 6, 8]
+    others = set(bench.WORKLOADS) - {bench.DEFAULT_WORKLOAD, "qwen2_57b_a14b_prefill2048"}
+    assert others == set(bench.SUB_WORKLOADS)
+    assert "internal.hpp" in " ".join(bench.ENGINE_SOURCES)
+
+
 def test_more_than_one_gpu_is_refused_with_a_message():
     r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)

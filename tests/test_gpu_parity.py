@@ -116,6 +116,35 @@ def test_group_single_expert_takes_every_token():
     assert int(nact.item()) == 1 and int(act[0].item()) == 5
 
 
+@pytest.mark.parametrize("T,E,k", [(5, 8, 4), (300, 64, 8), (3000, 64, 8), (40, 1024, 32), (700, 16, 16)])
+def test_group_by_expert_repeated_and_foreign_ids(T, E, k):
+    """Ids the routing never writes: a token naming one expert in several slots, and ids outside
+    [0, E) (-1, E, a large value).  The oracle's definition places every pair whose id names an
+    expert, stably by pair id (repeats in slot order), and leaves the others out; the kernel must
+    give the same offsets, placed pairs, active list and count."""
+    say(f"group foreign T={T} E={E} k={k}")
+    r = np.random.default_rng(T + E + 5 * k)
+    ids = r.integers(0, E, size=(T, k)).astype(np.int32)
+    rep = r.random((T, k)) < 0.3                                    # repeats inside tokens
+    for j in range(1, k):
+        ids[rep[:, j], j] = ids[rep[:, j], j - 1]
+    ids[r.random((T, k)) < 0.05] = -1
+    ids[r.random((T, k)) < 0.05] = E
+    ids[r.random((T, k)) < 0.02] = 1 << 20
+    ids[0, :] = ids[0, 0] if (0 <= ids[0, 0] < E) else 0            # one token naming one expert k times
+    ids[-1, -1] = -1                                                # at least one id of each foreign kind
+    ids[T // 2, 0] = E
+    ids[T // 2, k - 1] = 1 << 20
+    off, pairs, act, nact = _group_gpu(_t(ids), E)
+    r_off, r_pairs, r_act, r_n = oracle.group_by_expert(ids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), r_off)
+    n_placed = int(r_off[E])
+    assert n_placed < T * k
+    np.testing.assert_array_equal(pairs.cpu().numpy()[:n_placed], r_pairs)
+    np.testing.assert_array_equal(act.cpu().numpy(), r_act)
+    assert int(nact.item()) == r_n
+
+
 # ------------------------------------------------------------------------------------------
 # bit-plane decoding and the decode GEMV engine
 # ------------------------------------------------------------------------------------------
@@ -335,6 +364,91 @@ def test_invalid_descriptor_is_reported_not_read():
     apq.moe_check_device_error(ws)    # cleared by the read
 
 
+_ws_layers = {}
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (4, 60, 4), (11, 512, 10), (13, 1024, 32), (16, 60, 4),
+                                   (16, 1024, 32), (16, 8, 8), (17, 60, 4), (64, 512, 10), (2048, 64, 8)])
+@pytest.mark.parametrize("ties", [False, True], ids=["matmul", "ties"])
+def test_layer_workspace_routing_bit_exact(T, E, k, ties):
+    """The routing and grouping a moe_layer_forward call computes and leaves in its workspace --
+    top-k ids, gates, expert offsets and sorted pairs -- against the oracle, bit for bit (gates
+    within 1e-6).  Calls of at most 16 tokens run routing, grouping and the expert records in one
+    fused single-workgroup kernel (token x expert slot map); larger ones use the separate routing
+    and segmented grouping kernels.  Shapes cover both paths, E from 8 to 1024 and k up to 32;
+    "ties" rounds the logits to the fp16 grid and plants equal and signed-zero logits."""
+    say(f"layer workspace routing T={T} E={E} k={k} ties={ties}")
+    shape = wl.TINY.replace(H=128, E=E, I=128, k=k, T=T, name="workspace routing")
+    if E not in _ws_layers:
+        _ws_layers.clear()
+        _ws_layers[E] = gpu_layers.device_layer(shape)
+    dl = _ws_layers[E]
+    inputs = wl.gen_layer_inputs(shape)
+    logits = inputs.logits
+    if ties:
+        r = np.random.default_rng(T * 31 + E)
+        logits = (r.standard_normal((T, E)) * 2).astype(np.float16).astype(np.float32)
+        logits[0, : min(E, 3 * k)] = 0.5
+        if T > 1:
+            logits[1, ::2] = -0.0
+            logits[1, 1::2] = 0.0
+    y = torch.empty((T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(T, E, shape.H, shape.I, k, 0), dtype=torch.uint8, device=DEV)
+    apq.moe_layer_forward(_t(logits), _t(inputs.x), E, shape.H, shape.I, k, dl.table, y, ws)
+    apq.moe_check_device_error(ws)
+    view = apq.moe_workspace_routing(ws, T, E, shape.H, shape.I, k, 0)
+    ref_ids, ref_g = oracle.route_topk(logits, k)
+    np.testing.assert_array_equal(view["ids"].cpu().numpy().reshape(T, k), ref_ids)
+    np.testing.assert_allclose(view["gates"].cpu().numpy().reshape(T, k), ref_g, rtol=0, atol=1e-6)
+    r_off, r_pairs, _, _ = oracle.group_by_expert(ref_ids, E)
+    np.testing.assert_array_equal(view["offsets"].cpu().numpy(), r_off)
+    np.testing.assert_array_equal(view["pairs"].cpu().numpy(), r_pairs)
+
+
+def _expert_share(shape, inputs, get, e):
+    """Gate-weighted output of expert e for the tokens routed to it (float64 [T, H])."""
+    ids, gates = oracle.route_topk(inputs.logits, shape.k)
+    out = np.zeros((shape.T, shape.H))
+    t, j = np.nonzero(ids == e)
+    if len(t):
+        gi, gq, gl = get(e, wl.GATE_UP)
+        di, dq, dl_ = get(e, wl.DOWN)
+        o = oracle.expert_ffn(oracle.committed_index(gi, gq), gl, oracle.committed_index(di, dq), dl_,
+                              inputs.x[t].astype(np.float64))
+        out[t] = gates[t, j][:, None] * o
+    return out
+
+
+@pytest.mark.parametrize("threshold", [0, 1, 1000], ids=["auto", "all-mfma", "valu-max"])
+def test_skipped_expert_contributes_zero(threshold):
+    """A routed expert whose down block is not GPU-resident is skipped and reported; its tokens
+    keep their other experts' terms and the skipped expert adds exactly nothing, so y equals the
+    oracle's layer minus that expert's gate-weighted output."""
+    shape = wl.TINY.replace(H=256, E=8, I=256, k=2, T=21, I_shared=256, q_shared=8, name="skipped expert")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    ids, _ = oracle.route_topk(inputs.logits, shape.k)
+    e = int(np.bincount(ids.ravel(), minlength=shape.E).argmax())   # the busiest expert
+    table = dl.table.clone().view(torch.uint8).reshape(shape.E * 2, 32)
+    table[2 * e + 1, 26] = apq.MOE_PAGE_CPU                          # state byte of its down block
+    y = torch.empty((shape.T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.full((apq.moe_workspace_bytes(shape.T, shape.E, shape.H, shape.I, shape.k, shape.I_shared),),
+                    0x7F, dtype=torch.uint8, device=DEV)   # stale partial sums would show as NaN-like garbage
+    ws[:256].zero_()
+    apq.moe_layer_forward(_t(inputs.logits), _t(inputs.x), shape.E, shape.H, shape.I, shape.k,
+                          table.reshape(-1), y, ws, shared=dl.shared, I_shared=shape.I_shared,
+                          prefill_threshold=threshold)
+    with pytest.raises(apq.MoeError) as ei:
+        apq.moe_check_device_error(ws)
+    assert ei.value.code == apq.MOE_EDEVICE
+    get, sh = gpu_layers.oracle_getters(shape)
+    ref = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh)["y"]
+    ref = ref - _expert_share(shape, inputs, get, e)
+    err = oracle.rel_l2(y.float().cpu().numpy(), ref)
+    say(f"  expert {e} skipped: rel L2 {err:.2e}")
+    assert err <= LAYER_TOL
+
+
 def test_layer_replays_from_a_hip_graph():
     """moe_layer_forward issues no host synchronisation and no memset, so it can be captured;
     every replay (with other eager work between them) equals the eager call bit for bit."""
@@ -436,55 +550,136 @@ def test_routing_stats_from_a_layer_calls_workspace():
 
 
 # ------------------------------------------------------------------------------------------
-# width commits in the page table (lower by a prefix of planes; restore by an async copy)
+# page movement: width changes by a prefix of planes, eviction and return, async copies
 # ------------------------------------------------------------------------------------------
-def test_width_commit_lower_then_restore_asynchronously():
-    """One routed block goes from q=6 to q=3 by a commit of the same planes (its first 3 are the
-    width-3 planes) with the width-3 LUT: the layer then matches the oracle at width 3.  Its
-    tail planes are cleared (as if freed) and copied back from pinned host memory on another
-    stream while the layer keeps running at width 3 (same output bit for bit); a commit ordered
-    after the copy's event brings width 6 back and the layer matches the oracle again."""
-    shape = wl.TINY.replace(H=256, E=6, I=256, k=2, T=12, name="width commit")
+def _pinned(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).pin_memory()
+
+
+def _layer_unchecked(shape, inputs, dl):
+    """One layer call; returns (y float64, device error code or 0)."""
+    y = torch.empty((shape.T, shape.H), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(apq.moe_workspace_bytes(shape.T, shape.E, shape.H, shape.I, shape.k, shape.I_shared),
+                     dtype=torch.uint8, device=DEV)
+    apq.moe_layer_forward(_t(inputs.logits), _t(inputs.x), shape.E, shape.H, shape.I, shape.k, dl.table,
+                          y, ws, shared=dl.shared, I_shared=shape.I_shared)
+    code = 0
+    try:
+        apq.moe_check_device_error(ws)
+    except apq.MoeError as err:
+        code = err.code
+    return y.float().cpu().numpy().astype(np.float64), code
+
+
+def test_page_lower_width_then_reload_beside_layer_calls():
+    """A width change through the library's page calls (PagedWeight: nested widths, asynchronous
+    offload and reload, commits at safe boundaries).  One routed gate_up block goes from q = 6 to
+    q = 3 with moe_page_offload (same planes, the width-3 LUT already on the device): its planes
+    3..5 are copied to pinned host memory on a side stream, and the layer matches the oracle at
+    width 3.  Once the copy event has completed the freed planes are overwritten (reused).
+    moe_page_reload copies them back with the width-6 LUT on the side stream; a layer call
+    issued before the commit still runs at width 3 (bit for bit the same output); after
+    moe_page_commit the layer matches the oracle at width 6."""
+    shape = wl.TINY.replace(H=256, E=6, I=256, k=2, T=12, name="page width change")
     q6 = np.full((shape.E, 2), 6, dtype=np.uint8)
     inputs = wl.gen_layer_inputs(shape)
     dl = gpu_layers.device_layer(shape, q_override=q6)
     ids, _ = oracle.route_topk(inputs.logits, shape.k)
     e, m = int(ids[0, 0]), wl.GATE_UP
+    index = 2 * e + m
     blk = dl.block(e, m)
     idx8 = wl.gen_parent_indices(shape, e, m)
+    pb = blk.rows * blk.cols // 8
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
 
     def check(qmap):
-        y, _ = _run_layer(shape, inputs, dl)
+        y, code = _layer_unchecked(shape, inputs, dl)
+        assert code == 0
         get, sh = gpu_layers.oracle_getters(shape, qmap)
-        ref = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh)
-        err = oracle.rel_l2(y, ref["y"])
+        err = oracle.rel_l2(y, oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh)["y"])
         say(f"  widths of expert {e}: {qmap[e]}: rel L2 {err:.2e}")
         assert err <= LAYER_TOL
         return y
 
-    lut3 = torch.from_numpy(np.ascontiguousarray(wl.gen_lut(shape, e, m, 3), dtype=np.float16)).to(DEV)
+    lut3 = _t(np.ascontiguousarray(wl.gen_lut(shape, e, m, 3), dtype=np.float16).view(np.int16))
     low = apq.ApqBlock(blk.planes, lut3.data_ptr(), blk.rows, blk.cols, 3, 6, apq.MOE_PAGE_GPU, 0, 0)
-    apq.moe_commit_blocks(dl.table, [2 * e + m], [low])
+    host_planes = torch.zeros(6 * pb, dtype=torch.uint8).pin_memory()
+    apq.moe_page_offload(dl.table, index, blk, low, host_planes, None, ev, side)
     q3 = q6.copy()
     q3[e, m] = 3
     y3 = check(q3)
-
-    plane_bytes = blk.rows * blk.cols // 8
+    ev.synchronize()
+    packed = apq.moe_apq_pack(idx8, 6).view(np.uint8)
+    np.testing.assert_array_equal(host_planes.numpy()[3 * pb:], packed[3 * pb:])
     off = blk.planes - dl.arena.data_ptr()
-    tail = slice(off + 3 * plane_bytes, off + 6 * plane_bytes)
-    dl.arena[tail].zero_()
-    host_tail = torch.from_numpy(apq.moe_apq_pack(idx8, 6).view(np.uint8)[3 * plane_bytes: 6 * plane_bytes].copy()).pin_memory()
-    side = torch.cuda.Stream()
-    done = torch.cuda.Event()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        dl.arena[tail].copy_(host_tail, non_blocking=True)
-        done.record(side)
-    y3b, _ = _run_layer(shape, inputs, dl)       # still width 3 while the copy runs
+    dl.arena[off + 3 * pb: off + 6 * pb].fill_(0xA5)          # the freed planes are reused
+    torch.cuda.synchronize()
+
+    lut6_host = _pinned(np.ascontiguousarray(wl.gen_lut(shape, e, m, 6), dtype=np.float16).view(np.int16))
+    lut6_dev = torch.empty(blk.rows * 64, dtype=torch.int16, device=DEV)
+    tgt = apq.ApqBlock(blk.planes, lut6_dev.data_ptr(), blk.rows, blk.cols, 6, 6, apq.MOE_PAGE_GPU, 0, 0)
+    apq.moe_page_reload(dl.table, index, low, tgt, _pinned(packed), lut6_host, ev, side)
+    y3b, code = _layer_unchecked(shape, inputs, dl)          # before the commit: still width 3
+    assert code == 0
     np.testing.assert_array_equal(y3b, y3)
-    torch.cuda.current_stream().wait_event(done)
-    apq.moe_commit_blocks(dl.table, [2 * e + m], [blk])
+    apq.moe_page_commit(dl.table, index, tgt, ev)
     check(q6)
+
+
+def test_page_evict_to_host_and_bring_back():
+    """Eviction and return of a routed down block (PagedWeight: pages GPU-resident, CPU-resident
+    or in transfer).  moe_page_offload to MOE_PAGE_CPU copies its planes and LUT to pinned host
+    memory; layer calls then skip the expert, report MOE_EDEVICE, and give the oracle's layer
+    minus that expert's share.  The device memory is overwritten (reused), moe_page_reload brings
+    the block back from the host copies: until moe_page_commit the block is in transfer (same
+    skipped output, same report); after it the layer matches the oracle in full."""
+    shape = wl.TINY.replace(H=256, E=6, I=256, k=2, T=12, name="page evict")
+    q6 = np.full((shape.E, 2), 6, dtype=np.uint8)
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape, q_override=q6)
+    ids, _ = oracle.route_topk(inputs.logits, shape.k)
+    e = int(np.bincount(ids.ravel(), minlength=shape.E).argmax())
+    m = wl.DOWN
+    index = 2 * e + m
+    blk = dl.block(e, m)
+    pb = blk.rows * blk.cols // 8
+    lb = blk.rows * 64 * 2
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    get, sh = gpu_layers.oracle_getters(shape, q6)
+    full = oracle.layer_forward(inputs.x, inputs.logits, shape.k, get, shared=sh)["y"]
+    without = full - _expert_share(shape, inputs, get, e)
+
+    host_planes = torch.zeros(6 * pb, dtype=torch.uint8).pin_memory()
+    host_lut = torch.zeros(lb, dtype=torch.uint8).pin_memory()
+    evicted = apq.ApqBlock(blk.planes, blk.lut, blk.rows, blk.cols, 6, 6, apq.MOE_PAGE_CPU, 0, 0)
+    apq.moe_page_offload(dl.table, index, blk, evicted, host_planes, host_lut, ev, side)
+    y_out, code = _layer_unchecked(shape, inputs, dl)
+    assert code == apq.MOE_EDEVICE
+    err = oracle.rel_l2(y_out, without)
+    say(f"  expert {e} evicted: rel L2 vs the layer without it {err:.2e}")
+    assert err <= LAYER_TOL
+    ev.synchronize()
+    np.testing.assert_array_equal(host_planes.numpy(),
+                                  apq.moe_apq_pack(wl.gen_parent_indices(shape, e, m), 6).view(np.uint8))
+    np.testing.assert_array_equal(host_lut.numpy().view(np.float16),
+                                  np.ascontiguousarray(wl.gen_lut(shape, e, m, 6), dtype=np.float16).ravel())
+    po, lo = blk.planes - dl.arena.data_ptr(), blk.lut - dl.arena.data_ptr()
+    dl.arena[po: po + 6 * pb].fill_(0x5A)                     # the device pages are reused
+    dl.arena[lo: lo + lb].fill_(0x5A)
+    torch.cuda.synchronize()
+
+    apq.moe_page_reload(dl.table, index, evicted, blk, host_planes, host_lut, ev, side)
+    y_mid, code = _layer_unchecked(shape, inputs, dl)         # in transfer: still skipped
+    assert code == apq.MOE_EDEVICE
+    np.testing.assert_array_equal(y_mid, y_out)
+    apq.moe_page_commit(dl.table, index, blk, ev)
+    y_back, code = _layer_unchecked(shape, inputs, dl)
+    assert code == 0
+    err = oracle.rel_l2(y_back, full)
+    say(f"  expert {e} back: rel L2 {err:.2e}")
+    assert err <= LAYER_TOL
 
 
 # ------------------------------------------------------------------------------------------
@@ -571,6 +766,18 @@ def _lynx_gpu(logits, ids, bin_width=None):
     apq.moe_lynx_remap(_t(logits), ids, remapped, critical, bin_width=bin_width)
     torch.cuda.synchronize()
     return ids.cpu().numpy(), remapped.cpu().numpy(), critical.cpu().numpy().astype(bool)
+
+
+def test_lynx_negative_gap_on_gpu():
+    """Ids out of routing order (a negative top-2 gap) take bin 0 in the kernel as in the oracle:
+    the hand case of the oracle pins, through the kernel."""
+    logits = np.array([[2.0, 1.0, 0.5, 0.0, -1.0, -1.0],
+                       [0.5, -1.0, 3.0, 2.875, 0.0, -1.0]], dtype=np.float32)
+    ids = _t(np.array([[1, 0], [2, 3]], dtype=np.int32))
+    new, remapped, critical = _lynx_gpu(logits, ids)
+    np.testing.assert_array_equal(new, [[1, 2], [2, 1]])
+    np.testing.assert_array_equal(remapped, [[-1, 0], [-1, 3]])
+    np.testing.assert_array_equal(critical, [False, True, True, False, False, False])
 
 
 @pytest.mark.parametrize("T,E,k,kind", [(16, 60, 4, "matmul"), (64, 512, 10, "zipf"), (32, 8, 2, "matmul"),

@@ -89,8 +89,8 @@ def test_argument_validation_happens_before_any_launch():
                            fake, None, 0, None) == apq.MOE_EWORKSPACE
     assert lib.moe_layer_forward(fake, fake, 0, 8, 128, 256, 2, fake, None, 0, None, 0, fake, None, 0,
                                  None) == apq.MOE_OK                                     # T = 0
-    # LYNX remap: bin width must be positive and finite; outputs must be given
-    assert lib.moe_lynx_remap(fake, 4, 8, 2, 0.0, fake, fake, fake, None) == apq.MOE_EINVAL
+    # LYNX remap: bin width must be finite (<= 0 selects k/E); outputs must be given
+    assert lib.moe_lynx_remap(fake, 4, 8, 2, 0.0, fake, None, fake, None) == apq.MOE_EINVAL
     assert lib.moe_lynx_remap(fake, 4, 8, 2, float("nan"), fake, fake, fake, None) == apq.MOE_EINVAL
     assert lib.moe_lynx_remap(fake, 4, 8, 2, float("inf"), fake, fake, fake, None) == apq.MOE_EINVAL
     assert lib.moe_lynx_remap(fake, 4, 8, 2, 0.25, fake, None, fake, None) == apq.MOE_EINVAL
@@ -175,3 +175,132 @@ def test_native_width_planner_rejects_bad_arguments():
                 dict(mult=[0.0])):
         with pytest.raises(apq.MoeError):
             apq.moe_plan_widths(**{**ok, **bad}, target_bytes=1)
+
+
+def test_activation_arrays_of_4_gib_are_refused():
+    """The FFN kernels address x [T][H], act [T*k][I] and act_shared [T][I_shared] with 32-bit
+    byte offsets: a call whose arrays reach 4 GiB is refused with MOE_EUNSUPPORTED before any
+    launch (just below the limit it proceeds to the workspace check)."""
+    lib = apq.lib()
+    fake = 0x1000
+    T = 65536
+
+    def layer(H, I, k, Ish=0, shared=None):
+        return lib.moe_layer_forward(fake, fake, T, 64, H, I, k, fake, shared, Ish, None, 0, fake, fake,
+                                     1 << 20, None)
+
+    assert layer(32768, 128, 2) == apq.MOE_EUNSUPPORTED                  # x: T*H*2 = 4 GiB
+    assert layer(32640, 128, 2) == apq.MOE_EWORKSPACE                    # x just below
+    assert layer(4096, 8192, 8) == apq.MOE_EUNSUPPORTED                  # act: 8.6 GB
+    assert layer(4096, 1024, 32) == apq.MOE_EUNSUPPORTED                 # act: exactly 4 GiB
+    assert layer(4096, 896, 32) == apq.MOE_EWORKSPACE                    # act: 3.76 GB
+    assert layer(4096, 128, 2, Ish=32768, shared=fake) == apq.MOE_EUNSUPPORTED   # act_shared
+    assert b"4 GiB" in lib.moe_last_error()
+    assert lib.moe_apq_ffn(fake, 64, 4096, 8192, fake, T, 8, fake, fake, fake, fake, fake, None, 0, None,
+                           0, fake, fake, 1 << 20, None) == apq.MOE_EUNSUPPORTED
+    blk = apq.ApqBlock(fake, fake, 64, 32768, 4, 4, 0, 0, 0)
+    assert lib.moe_apq_gemv(apq.ctypes.byref(blk), fake, T, fake, 0, None) == apq.MOE_EUNSUPPORTED
+
+
+def test_commit_refuses_indices_outside_the_table_and_repeats():
+    """moe_commit_blocks knows the table's length: an index past it, or one entry named twice in
+    one commit (whose winner would depend on thread timing), is refused before any launch."""
+    lib = apq.lib()
+    fake = 0x1000
+    ok = apq.ApqBlock(fake, fake, 64, 128, 4, 4, 0, 0, 0)
+
+    def commit(index, table_len=8):
+        n = len(index)
+        idx = (apq.ctypes.c_int32 * n)(*index)
+        arr = (apq.ApqBlock * n)(*([ok] * n))
+        return lib.moe_commit_blocks(fake, table_len, idx, arr, n, None)
+
+    assert commit([8]) == apq.MOE_EINVAL
+    assert b"outside the table" in lib.moe_last_error()
+    assert commit([-1]) == apq.MOE_EINVAL
+    assert commit([3, 5, 3]) == apq.MOE_EINVAL
+    assert b"repeats" in lib.moe_last_error()
+    assert commit([0], table_len=0) == apq.MOE_EINVAL
+    assert lib.moe_commit_blocks(fake, 8, None, None, 0, None) == apq.MOE_OK   # nothing to do
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except ImportError:  # pragma: no cover
+        return False
+
+
+def test_page_state_machine_allows_exactly_the_documented_moves():
+    """The host rules of moe_page_reload / moe_page_offload over every (current state, target
+    state, width step, planes, LUT) combination: a move the rules forbid is refused with
+    MOE_EINVAL before anything is issued; an allowed one passes validation and reaches its first
+    device call (on a machine without a GPU that call fails with MOE_EHIP, which is how the test
+    tells the two apart).  Allowed: GPU -> GPU at a higher width (same planes, new LUT), CPU ->
+    GPU (through IN_TRANSFER); GPU -> CPU, GPU -> GPU at a lower width (same planes).  Refused:
+    anything from IN_TRANSFER, a reload to a width that does not grow or with other planes or
+    the LUT still in use, an offload to a width that does not shrink, to IN_TRANSFER or of a
+    block that is not resident."""
+    if _gpu_visible():
+        pytest.skip("the allowed moves would launch on the GPU with made-up pointers")
+    lib = apq.lib()
+    byref = apq.ctypes.byref
+    P0, P1, L0, L1, fake = 0x10000, 0x20000, 0x30000, 0x40000, 0x1000
+    GPU, CPU, XFER = apq.MOE_PAGE_GPU, apq.MOE_PAGE_CPU, apq.MOE_PAGE_IN_TRANSFER
+
+    def blk(planes, lut, q, state):
+        return apq.ApqBlock(planes, lut, 64, 128, q, q, state, 0, 0)
+
+    def reload(cur, tgt, index=1):
+        return lib.moe_page_reload(fake, 4, index, byref(cur), byref(tgt), fake, fake, fake, None, None)
+
+    def offload(cur, tgt, index=1):
+        return lib.moe_page_offload(fake, 4, index, byref(cur), byref(tgt), fake, fake, fake, None, None)
+
+    allowed = apq.MOE_EHIP
+    # reloads
+    assert reload(blk(P0, L0, 3, GPU), blk(P0, L1, 6, GPU)) == allowed      # raise the width
+    assert reload(blk(P0, L0, 6, CPU), blk(P0, L1, 6, GPU)) == allowed      # bring back
+    assert reload(blk(P0, L0, 6, CPU), blk(P1, L1, 8, GPU)) == allowed      # to a new place
+    assert reload(blk(P0, L0, 6, XFER), blk(P0, L1, 6, GPU)) == apq.MOE_EINVAL
+    assert b"already in transfer" in lib.moe_last_error()
+    assert reload(blk(P0, L0, 6, GPU), blk(P0, L1, 6, GPU)) == apq.MOE_EINVAL   # no growth
+    assert reload(blk(P0, L0, 6, GPU), blk(P0, L1, 4, GPU)) == apq.MOE_EINVAL
+    assert reload(blk(P0, L0, 3, GPU), blk(P1, L1, 6, GPU)) == apq.MOE_EINVAL   # other planes
+    assert reload(blk(P0, L0, 3, GPU), blk(P0, L0, 6, GPU)) == apq.MOE_EINVAL   # LUT in use
+    assert reload(blk(P0, L0, 3, CPU), blk(P0, L1, 6, CPU)) == apq.MOE_EINVAL   # target not GPU
+    assert reload(blk(P0, L0, 3, CPU), blk(P0, L1, 6, XFER)) == apq.MOE_EINVAL
+    assert reload(blk(P0, L0, 3, CPU), blk(P0, L1, 9, GPU)) == apq.MOE_EINVAL   # q outside 1..8
+    assert reload(blk(P0, L0, 3, CPU), blk(P0, L1, 6, GPU), index=4) == apq.MOE_EINVAL
+    odd = apq.ApqBlock(P0, L1, 64, 256, 6, 6, GPU, 0, 0)
+    assert reload(blk(P0, L0, 3, GPU), odd) == apq.MOE_EINVAL                   # other shape
+    # offloads
+    assert offload(blk(P0, L0, 6, GPU), blk(P0, L0, 6, CPU)) == allowed     # evict
+    assert offload(blk(P0, L0, 6, GPU), blk(P0, L1, 3, GPU)) == allowed     # lower the width
+    assert offload(blk(P0, L0, 6, CPU), blk(P0, L0, 6, CPU)) == apq.MOE_EINVAL  # not resident
+    assert offload(blk(P0, L0, 6, XFER), blk(P0, L0, 6, CPU)) == apq.MOE_EINVAL
+    assert offload(blk(P0, L0, 6, GPU), blk(P0, L1, 6, GPU)) == apq.MOE_EINVAL  # no shrink
+    assert offload(blk(P0, L0, 6, GPU), blk(P0, L1, 8, GPU)) == apq.MOE_EINVAL
+    assert offload(blk(P0, L0, 6, GPU), blk(P1, L1, 3, GPU)) == apq.MOE_EINVAL  # other planes
+    assert offload(blk(P0, L0, 6, GPU), blk(P0, L1, 3, XFER)) == apq.MOE_EINVAL
+    assert offload(blk(P0, L0, 6, GPU), blk(P0, L0, 6, CPU), index=-1) == apq.MOE_EINVAL
+    # the commit that ends a reload: a resident target inside the table
+    def commit(tgt, index=1):
+        return lib.moe_page_commit(fake, 4, index, byref(tgt), fake, None)
+
+    assert commit(blk(P0, L1, 6, GPU)) == allowed
+    assert commit(blk(P0, L1, 6, CPU)) == apq.MOE_EINVAL
+    assert commit(blk(P0, L1, 6, XFER)) == apq.MOE_EINVAL
+    assert commit(blk(P0, L1, 6, GPU), index=4) == apq.MOE_EINVAL
+    assert commit(blk(P0, L1, 0, GPU)) == apq.MOE_EINVAL
+    # a full cycle of one block: GPU(6) -> GPU(3) -> CPU -> (IN_TRANSFER) -> GPU(6) -> GPU(8);
+    # each step validated against the descriptor the previous step committed
+    seq = [(offload, blk(P0, L0, 6, GPU), blk(P0, L1, 3, GPU)),
+           (offload, blk(P0, L1, 3, GPU), blk(P0, L1, 3, CPU)),
+           (reload, blk(P0, L1, 3, CPU), blk(P0, L0, 6, GPU)),
+           (reload, blk(P0, L0, 6, GPU), blk(P0, L1, 8, GPU))]
+    for fn, cur, tgt in seq:
+        assert fn(cur, tgt) == allowed, lib.moe_last_error()
+        if fn is reload:
+            assert commit(tgt) == allowed, lib.moe_last_error()

@@ -594,6 +594,28 @@ def test_lynx_bin_boundaries_and_quotient_rounding():
         assert np.float32(c / ww) == np.float32(float(c) / float(ww))
 
 
+def test_lynx_negative_gap_counts_as_bin_zero():
+    """Slots handed over out of routing order (the caller's ids, e.g. after its own edits) give a
+    negative top-2 gap; the reading takes such a token as least confident: bin 0, one critical
+    slot (its slot 0).  Hand-derived: E = 6, k = 2, w = 1/3.  Token 0 names [1, 0] with logits
+    1.0 and 2.0: gap -1.0, quotient -3 -> bin 0, keeps slot 0 (expert 1).  Token 1 names [2, 3]
+    (logits 3.0, 2.875): gap 0.125 -> bin 0, keeps expert 2.  Critical set {1, 2}.  Token 0's
+    slot 1 (expert 0, not critical) takes the best critical expert it does not hold: 2; token
+    1's slot 1 (expert 3) takes 1."""
+    logits = np.array([[2.0, 1.0, 0.5, 0.0, -1.0, -1.0],
+                       [0.5, -1.0, 3.0, 2.875, 0.0, -1.0]], dtype=np.float32)
+    ids = np.array([[1, 0], [2, 3]], dtype=np.int32)
+    w = np.float32(2) / np.float32(6)
+    conf, bins, keep = oracle.lynx_bins(logits, ids, w)
+    np.testing.assert_array_equal(conf, np.array([-1.0, 0.125], dtype=np.float32))
+    np.testing.assert_array_equal(bins, [0, 0])
+    np.testing.assert_array_equal(keep, [1, 1])
+    new, remapped, critical = oracle.lynx_remap(logits, ids, w)
+    np.testing.assert_array_equal(new, [[1, 2], [2, 1]])
+    np.testing.assert_array_equal(remapped, [[-1, 0], [-1, 3]])
+    np.testing.assert_array_equal(critical, [False, True, True, False, False, False])
+
+
 def test_lynx_remap_invariants_and_brute_force_choice():
     """Random batches: every token keeps k distinct experts; its first `keep` slots are
     unchanged; a remapped slot held a non-critical expert and now holds the highest-logit
