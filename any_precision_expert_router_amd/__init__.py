@@ -27,7 +27,7 @@ MOE_PAGE_GPU, MOE_PAGE_CPU, MOE_PAGE_IN_TRANSFER = 0, 1, 2
 GATE_UP, DOWN = 0, 1
 
 EXPORTED = (
-    "moe_route_topk", "moe_group_by_expert", "moe_apq_ffn", "moe_layer_forward",
+    "moe_route_topk", "moe_group_by_expert", "moe_apq_ffn", "moe_layer_forward", "moe_layer_forward_noalloc",
     "moe_workspace_bytes", "moe_apq_pack", "moe_apq_gemv", "moe_apq_decode_indices",
     "moe_check_device_error", "moe_profile_start", "moe_profile_stop", "moe_hbm_read_probe",
     "moe_routing_stats", "moe_workspace_routing", "moe_commit_blocks", "moe_plan_widths",
@@ -73,6 +73,7 @@ def _load():
         "moe_group_by_expert": ([P, I, I, I, P, P, P, P, P, Z, S], I),
         "moe_apq_ffn": ([P, I, I, I, P, I, I, P, P, P, P, P, P, I, P, I, P, P, Z, S], I),
         "moe_layer_forward": ([P, P, I, I, I, I, I, P, P, I, P, I, P, P, Z, S], I),
+        "moe_layer_forward_noalloc": ([P, P, I, I, I, I, I, P, P, I, P, I, P, P, S], I),
         "moe_workspace_bytes": ([I, I, I, I, I, I], Z),
         "moe_apq_pack": ([P, I, I, I, P], I),
         "moe_apq_gemv": ([P, P, I, P, I, S], I),
@@ -163,6 +164,20 @@ def moe_layer_forward(logits, x, E: int, H: int, I: int, k: int, table, y, works
         _ptr(logits), _ptr(x), T, E, H, I, k, _ptr(table), _ptr(shared), I_shared,
         _ptr(shared_scale), prefill_threshold, _ptr(y), _ptr(workspace), workspace.numel(),
         _stream(stream)))
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20   # MOE_NOALLOC_WORKSPACE_BYTES
+
+
+def moe_layer_forward_noalloc(logits, x, E: int, H: int, I: int, k: int, table, y, status=None,
+                              shared=None, I_shared: int = 0, shared_scale=None,
+                              prefill_threshold: int = 0, stream=None) -> None:
+    """The whole layer on the library's own device array (no workspace argument; nothing is
+    allocated).  status: optional device int32 [1] that receives the call's error word."""
+    T = x.shape[0]
+    _check("moe_layer_forward_noalloc", _lib.moe_layer_forward_noalloc(
+        _ptr(logits), _ptr(x), T, E, H, I, k, _ptr(table), _ptr(shared), I_shared,
+        _ptr(shared_scale), prefill_threshold, _ptr(y), _ptr(status), _stream(stream)))
 
 
 def moe_workspace_bytes(T: int, E: int, H: int, I: int, k: int, I_shared: int = 0) -> int:

@@ -72,6 +72,9 @@ ProfileScope::~ProfileScope() {
   if (slot_ >= 0) (void)hipEventRecord(g_prof.recs[slot_].stop, stream_);
 }
 
+ProfilePause::ProfilePause() : was_on_(g_prof.on) { g_prof.on = false; }
+ProfilePause::~ProfilePause() { g_prof.on = was_on_; }
+
 int device_cu_count() {
   static int cache[64] = {0};
   int dev = 0;
@@ -185,6 +188,38 @@ int check_ffn_range(int T, int H, int I, int k, int I_shared) {
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
+
+int check_layer_args(const float* logits, const uint16_t* x, int T, int E, int H, int I, int k,
+                     const moe_apq_block* table, const moe_apq_block* shared, int I_shared, uint16_t* y) {
+  if (int rc = check_route_args(T, E, k)) return rc;
+  if (int rc = check_ffn_dims(H, I, I_shared, shared != nullptr)) return rc;
+  if (T == 0) return MOE_OK;
+  if (!logits || !x || !table || !y) return set_error(MOE_EINVAL, "NULL pointer argument");
+  return check_ffn_range(T, H, I, k, shared ? I_shared : 0);
+}
+
+int layer_forward_ws(const float* logits, const uint16_t* x, int T, int E, int H, int I, int k,
+                     const moe_apq_block* table, const moe_apq_block* shared, int I_shared,
+                     const float* shared_scale, int prefill_threshold, uint16_t* y, const Workspace& ws,
+                     bool clear_err, int32_t* status, hipStream_t s) {
+  const int ish = shared ? I_shared : 0;
+  RecordArgs ra{table, shared, ws.gates, E, H, I, ish, T, k, ws.recs, ws.counters, ws.n_recs,
+                effective_dense_threshold(prefill_threshold)};
+  ra.err_clear = clear_err ? ws.err : nullptr;
+  if (T <= kFusedRouteMaxT && static_cast<long>(T) * k <= kFusedRouteMaxPairs) {
+    if (int rc = launch_route_group_records(logits, ws.ids, ws.gates, ws.offsets, ws.pairs, ws.active,
+                                            ws.n_active, ra, s))
+      return rc;
+  } else {
+    if (int rc = launch_route_topk(logits, T, E, k, ws.ids, ws.gates, s)) return rc;
+    if (int rc = launch_group_records(ws.ids, ws.offsets, ws.pairs, ws.active, ws.n_active, ra, s))
+      return rc;
+  }
+  FfnArgs a{table, shared, E, H, I, k, T, ish, x, ws.offsets, ws.pairs, ws.active, ws.n_active,
+            ws.gates, shared_scale, y, ws, prefill_threshold};
+  a.status = status;
+  return launch_apq_ffn(a, s);
+}
 }  // namespace moeapq
 
 using namespace moeapq;
@@ -253,31 +288,15 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int T, int E, int 
                       const float* shared_scale, int prefill_threshold, uint16_t* y,
                       void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
-  if (int rc = check_route_args(T, E, k)) return rc;
-  if (int rc = check_ffn_dims(H, I, I_shared, shared != nullptr)) return rc;
+  if (int rc = check_layer_args(logits, x, T, E, H, I, k, table, shared, I_shared, y)) return rc;
   if (T == 0) return MOE_OK;
-  if (!logits || !x || !table || !y) return set_error(MOE_EINVAL, "NULL pointer argument");
   const int ish = shared ? I_shared : 0;
-  if (int rc = check_ffn_range(T, H, I, k, ish)) return rc;
   const Workspace ws = carve_workspace(workspace, T, E, H, I, k, ish);
   if (!workspace || ws_bytes < ws.bytes)
     return set_error(MOE_EWORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
                      ws.bytes);
-  hipStream_t s = as_stream(stream);
-  const RecordArgs ra{table, shared, ws.gates, E, H, I, ish, T, k, ws.recs, ws.counters, ws.n_recs,
-                      effective_dense_threshold(prefill_threshold)};
-  if (T <= kFusedRouteMaxT && static_cast<long>(T) * k <= kFusedRouteMaxPairs) {
-    if (int rc = launch_route_group_records(logits, ws.ids, ws.gates, ws.offsets, ws.pairs, ws.active,
-                                            ws.n_active, ra, s))
-      return rc;
-  } else {
-    if (int rc = launch_route_topk(logits, T, E, k, ws.ids, ws.gates, s)) return rc;
-    if (int rc = launch_group_records(ws.ids, ws.offsets, ws.pairs, ws.active, ws.n_active, ra, s))
-      return rc;
-  }
-  FfnArgs a{table, shared, E, H, I, k, T, ish, x, ws.offsets, ws.pairs, ws.active, ws.n_active,
-            ws.gates, shared_scale, y, ws, prefill_threshold};
-  return launch_apq_ffn(a, s);
+  return layer_forward_ws(logits, x, T, E, H, I, k, table, shared, I_shared, shared_scale, prefill_threshold,
+                          y, ws, false, nullptr, as_stream(stream));
 }
 
 int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float* y,

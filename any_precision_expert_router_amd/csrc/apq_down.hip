@@ -9,8 +9,12 @@ namespace {
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part,
                                                       const float* __restrict__ part_shared, int T,
                                                       int H, int k, int segs, int segs_shared,
-                                                      uint16_t* __restrict__ y) {
+                                                      uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ err,
+                                                      int32_t* __restrict__ status) {
   const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  // the FFN launches of this call ran before: their error word is final
+  if (status && i == 0) *status = err[0];
   const size_t TH = static_cast<size_t>(T) * H;
   if (i >= TH) return;
   const size_t t = i / H, r = i - t * H;
@@ -33,11 +37,12 @@ int launch_down(const KArgs& k, int max_items, hipStream_t stream) {
 }
 
 int launch_combine(const float* part, const float* part_shared, int T, int H, int k, int segs,
-                   int segs_shared, uint16_t* y, hipStream_t stream) {
+                   int segs_shared, uint16_t* y, const int32_t* err, int32_t* status,
+                   hipStream_t stream) {
   const size_t n = static_cast<size_t>(T) * H;
   ProfileScope prof("combine", stream);
   hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     stream, part, part_shared, T, H, k, segs, segs_shared, y);
+                     stream, part, part_shared, T, H, k, segs, segs_shared, y, err, status);
   return check_launch("combine");
 }
 }  // namespace apq

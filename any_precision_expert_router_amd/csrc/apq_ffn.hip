@@ -7,7 +7,8 @@ namespace apq {
 int launch_gate_up(const KArgs& k, int max_items, hipStream_t stream);
 int launch_down(const KArgs& k, int max_items, hipStream_t stream);
 int launch_combine(const float* part, const float* part_shared, int T, int H, int k, int segs,
-                   int segs_shared, uint16_t* y, hipStream_t stream);
+                   int segs_shared, uint16_t* y, const int32_t* err, int32_t* status,
+                   hipStream_t stream);
 int launch_plain(const KArgs& k, int max_items, hipStream_t stream);
 int launch_decode(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
 }  // namespace apq
@@ -38,7 +39,7 @@ int launch_apq_ffn(const FfnArgs& a, hipStream_t stream) {
   const int dn_items = (sh * k.segs_shared + routed * k.segs) * (a.H / kRowPanel);
   if (int rc = apq::launch_down(k, dn_items, stream)) return rc;
   return apq::launch_combine(a.ws.part, sh ? a.ws.part_shared : nullptr, a.T, a.H, a.k, k.segs,
-                             k.segs_shared, a.y, stream);
+                             k.segs_shared, a.y, a.ws.err, a.status, stream);
 }
 
 int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y,

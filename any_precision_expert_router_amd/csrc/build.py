@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libmoe_apq.so"
 SOURCES = ["apq_gate_up.hip", "apq_down.hip", "apq_plain.hip", "abi.hip", "route.hip", "apq_ffn.hip",
-           "probe.hip", "stats.hip", "pages.hip", "substitute.hip", "lynx.hip",
+           "probe.hip", "stats.hip", "pages.hip", "substitute.hip", "lynx.hip", "scratch.hip",
            "pack.cpp", "planner.cpp"]
 ARCH = os.environ.get("MOE_APQ_ARCH", "gfx950")
 

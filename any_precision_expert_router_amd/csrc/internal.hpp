@@ -25,6 +25,13 @@ struct ProfileScope {
   hipStream_t stream_;
   int slot_;
 };
+// Suspends the timer on this thread for its lifetime (an entry point that must not create
+// events, which the timer does on first use).
+struct ProfilePause {
+  ProfilePause();
+  ~ProfilePause();
+  bool was_on_;
+};
 
 // ---- device facts ---------------------------------------------------------------------------
 int device_cu_count();  // compute units of the current device (cached per device)
@@ -137,6 +144,7 @@ struct RecordArgs {
   uint32_t* counters;
   int32_t* n_recs;             // out: routed records written (records 1 .. n_recs)
   int dense_threshold;         // the FFN's effective threshold (orders the records)
+  int32_t* err_clear = nullptr;  // non-null: the device error word, cleared at the call's start
 };
 // Routing, grouping and the records in one single-workgroup launch (small batches).
 constexpr int kFusedRouteMaxT = 16;   // one token per wavefront of the fused workgroup
@@ -165,8 +173,17 @@ struct FfnArgs {
   uint16_t* y;
   Workspace ws;
   int dense_threshold;  // <= 0: library default
+  int32_t* status = nullptr;  // non-null: device int32 that receives the error word at the end
 };
 int launch_apq_ffn(const FfnArgs& a, hipStream_t stream);
+// The whole layer on a carved workspace (moe_layer_forward and its allocation-free variant).
+int layer_forward_ws(const float* logits, const uint16_t* x, int T, int E, int H, int I, int k,
+                     const moe_apq_block* table, const moe_apq_block* shared, int I_shared,
+                     const float* shared_scale, int prefill_threshold, uint16_t* y, const Workspace& ws,
+                     bool clear_err, int32_t* status, hipStream_t stream);
+// Argument checks shared by the layer entry points (host scalars only).
+int check_layer_args(const float* logits, const uint16_t* x, int T, int E, int H, int I, int k,
+                     const moe_apq_block* table, const moe_apq_block* shared, int I_shared, uint16_t* y);
 int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y,
                     int dense_threshold, hipStream_t stream);
 

@@ -427,6 +427,7 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
     r.recs[0] = rec;
   }
   for (int c = tid; c < kNumCounters; c += blockDim.x) r.counters[c] = 0u;
+  if (r.err_clear && tid < 3) r.err_clear[tid] = 0;   // the FFN launches of this call set it
 }
 
 // Routing of up to kFusedRouteMaxT tokens by the 16 wavefronts of one workgroup, then grouping

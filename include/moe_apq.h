@@ -173,6 +173,28 @@ int moe_layer_forward(const float* logits, const uint16_t* x, int T, int E, int 
                       const float* shared_scale, int prefill_threshold, uint16_t* y,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * The whole layer without a workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   Same arguments and results as moe_layer_forward; the workspace is a fixed device array of
+ *   MOE_NOALLOC_WORKSPACE_BYTES inside the library (one per GPU, held until the process ends),
+ *   so the call allocates nothing.  A call whose moe_workspace_bytes() exceeds that size is
+ *   refused with MOE_EWORKSPACE before anything is issued (every decode shape of the pages'
+ *   models fits; a 2048-token prefill chunk does not: use moe_layer_forward).
+ *   status: device int32 [1] or NULL.  The call clears its device error word when it starts and
+ *   writes it to *status when it ends (0 = clean; nonzero = a routed block was skipped, as
+ *   moe_check_device_error reports for moe_layer_forward).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ *   other threads) race and their results are undefined; order them on one stream.  The array
+ *   keeps the last call's contents.  Errors: as moe_layer_forward, MOE_EWORKSPACE above the limit,
+ *   MOE_EHIP if the array's device address cannot be obtained.
+ */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+int moe_layer_forward_noalloc(const float* logits, const uint16_t* x, int T, int E, int H, int I, int k,
+                              const moe_apq_block* table, const moe_apq_block* shared, int I_shared,
+                              const float* shared_scale, int prefill_threshold, uint16_t* y,
+                              int32_t* status, void* stream);
+
 /* Workspace bytes moe_apq_ffn / moe_layer_forward need for these sizes (0 on bad arguments). */
 size_t moe_workspace_bytes(int T, int E, int H, int I, int k, int I_shared);
 
