@@ -53,7 +53,6 @@ MOE_INLINE const AS_CONST T* cview(const void* p) { return (const AS_CONST T*)p;
 constexpr int kThreads = 64 * kWavesPerTile;
 constexpr int kMaxTokGroup = 4;                  // tokens sharing one VALU pass over the weights
 constexpr int kDenseGroup = 16;                  // tokens per MFMA pass (32x32 tile: 2 row halves x 16)
-static_assert(kDenseGroup == kRecGroupTok, "a split record holds one matrix-core token group");
 
 // LDS map of a tile workgroup (bytes):
 //   [0, 64K)        lookup tables, 4-byte slots [entry][64 lanes] unless noted.  Streaming (VALU)
@@ -633,29 +632,61 @@ MOE_INLINE uint32_t lds_u16(uint32_t byte_addr) {
   return *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(g_lds) + byte_addr);
 }
 
-// One 32-column word through the dense table: dword 4b + j = (column 8b + 2j, column 8b + 2j + 1).
+// One 32-column word through the dense table, in two phases so that a word's LDS lookups can be
+// in flight while other work issues: dense_lookup issues every lookup of the word (16 for the
+// pair table, 32 for the single tables) into `v`, dense_finish turns them into the 16 dwords
+// wv[4b + j] = (column 8b + 2j, column 8b + 2j + 1).  Keeping the lookups together matters: when
+// they are interleaved with their uses, every pair of lookups waits out the full LDS latency.
 template <int Q>
-MOE_INLINE void decode_word_dense(const uint32_t (&w)[Q], uint32_t lane4, uint32_t (&wv)[16]) {
+MOE_INLINE void dense_lookup(const uint32_t (&w)[Q], uint32_t lane4, uint32_t (&v)[32]) {
   if constexpr (dense_table_kind<Q>() == 0) {
-    decode_word<Q>(w, lane4, wv);
+    uint32_t pw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pw[j] = pair_word<Q>(w, j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) v[4 * b + j] = lds_load(tbl_addr(pw[j], lane4, b));
   } else {
+    uint32_t sw[8];
+#pragma unroll
+    for (int o = 0; o < 8; ++o) sw[o] = single_word<Q>(w, o);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t we = single_word<Q>(w, j), wo = single_word<Q>(w, j + 4);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if constexpr (dense_table_kind<Q>() == 2) {
-          const uint32_t lo = lds_u16(tbl_addr(we, lane4, b) >> 1);
-          const uint32_t hi = lds_u16(tbl_addr(wo, lane4, b) >> 1);
-          wv[4 * b + j] = lo | (hi << 16);
+          v[4 * b + j] = lds_u16(tbl_addr(sw[j], lane4, b) >> 1);
+          v[16 + 4 * b + j] = lds_u16(tbl_addr(sw[j + 4], lane4, b) >> 1);
         } else {
-          const uint32_t ve = lds_load(tbl_addr(we, lane4, b));
-          const uint32_t vo = lds_load(tbl_addr(wo, lane4, b));
-          wv[4 * b + j] = __builtin_amdgcn_perm(vo, ve, 0x05040100u);  // (even lo, odd hi)
+          v[4 * b + j] = lds_load(tbl_addr(sw[j], lane4, b));
+          v[16 + 4 * b + j] = lds_load(tbl_addr(sw[j + 4], lane4, b));
         }
       }
     }
   }
+}
+
+template <int Q>
+MOE_INLINE void dense_finish(const uint32_t (&v)[32], uint32_t (&wv)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (dense_table_kind<Q>() == 0) {
+      wv[i] = v[i];
+    } else if constexpr (dense_table_kind<Q>() == 2) {
+      wv[i] = v[i] | (v[16 + i] << 16);
+    } else {
+      wv[i] = __builtin_amdgcn_perm(v[16 + i], v[i], 0x05040100u);  // (even lo, odd hi)
+    }
+  }
+}
+
+template <int Q>
+MOE_INLINE void decode_word_dense(const uint32_t (&w)[Q], uint32_t lane4, uint32_t (&wv)[16]) {
+  uint32_t v[32];
+  dense_lookup<Q>(w, lane4, v);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_finish<Q>(v, wv);
 }
 
 // 16 bytes per lane from `rsrc` at voff + soff straight into LDS at m0 + 16 * lane.  The
@@ -717,14 +748,30 @@ MOE_INLINE void dense_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * Q + DenseStream<Q>::kDma) : "memory");
 }
 
+// A word's operands in flight: its two B operands (the staged activations of octets 4 JW ..
+// 4 JW + 3) and its table lookups.  The B reads go first: LDS operations complete in order, so
+// the products of this word then never wait for the lookups of the word issued after them.
+template <int Q>
+struct DenseWordOps {
+  u32x4 b[2];
+  uint32_t v[32];
+};
+
 template <int Q, int JW>
-MOE_INLINE void dense_word(const DenseStream<Q>& S, int s, uint32_t lane4, f32x16& lo, f32x16& hi) {
+MOE_INLINE void dense_word_lookup(const DenseStream<Q>& S, int s, uint32_t lane4, DenseWordOps<Q>& o) {
+  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kXSlotBytes;
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr) o.b[pr] = *reinterpret_cast<const u32x4*>(xb + (JW * 4 + 2 * pr) * 256);
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = word_of(S.buf[s][p], JW);
+  dense_lookup<Q>(w, lane4, o.v);
+}
+
+template <int Q>
+MOE_INLINE void dense_word_mma(const DenseWordOps<Q>& o, f32x16& lo, f32x16& hi) {
   uint32_t wv[16];
-  decode_word_dense<Q>(w, lane4, wv);
-  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kXSlotBytes;
+  dense_finish<Q>(o.v, wv);
 #pragma unroll
   for (int pr = 0; pr < 2; ++pr) {
     // octets o = 2 pr and o + 1 of this word: columns 16 pr .. 16 pr + 15
@@ -735,13 +782,33 @@ MOE_INLINE void dense_word(const DenseStream<Q>& S, int s, uint32_t lane4, f32x1
       a1[r] = sw[0];
       a2[r] = sw[1];
     }
-    const u32x4 b = *reinterpret_cast<const u32x4*>(xb + (JW * 4 + 2 * pr) * 256);
     const u32x4 va1 = {a1[0], a1[1], a1[2], a1[3]}, va2 = {a2[0], a2[1], a2[2], a2[3]};
     lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va1),
-                                                 __builtin_bit_cast(half8_t, b), lo, 0, 0, 0);
+                                                 __builtin_bit_cast(half8_t, o.b[pr]), lo, 0, 0, 0);
     hi = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va2),
-                                                 __builtin_bit_cast(half8_t, b), hi, 0, 0, 0);
+                                                 __builtin_bit_cast(half8_t, o.b[pr]), hi, 0, 0, 0);
   }
+}
+
+// The four words of ring slot s, software-pipelined: word j + 1's lookups are issued before
+// word j's products, so the LDS latency overlaps the previous word's matrix-core work.
+template <int Q>
+MOE_INLINE void dense_chunk(const DenseStream<Q>& S, int s, uint32_t lane4, f32x16& lo, f32x16& hi) {
+  DenseWordOps<Q> a, b;
+  dense_word_lookup<Q, 0>(S, s, lane4, a);
+  dense_word_lookup<Q, 1>(S, s, lane4, b);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_word_mma<Q>(a, lo, hi);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_word_lookup<Q, 2>(S, s, lane4, a);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_word_mma<Q>(b, lo, hi);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_word_lookup<Q, 3>(S, s, lane4, b);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_word_mma<Q>(a, lo, hi);
+  __builtin_amdgcn_sched_barrier(0);
+  dense_word_mma<Q>(b, lo, hi);
 }
 
 template <int Q>
@@ -753,10 +820,7 @@ MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& lo, f32
       const int c = c0 + s;
       if (c < S.ce) {
         dense_wait<Q>();
-        dense_word<Q, 0>(S, s, lane4, lo, hi);
-        dense_word<Q, 1>(S, s, lane4, lo, hi);
-        dense_word<Q, 2>(S, s, lane4, lo, hi);
-        dense_word<Q, 3>(S, s, lane4, lo, hi);
+        dense_chunk<Q>(S, s, lane4, lo, hi);
         S.issue(s, S.clamp(c + D));
       }
     }
@@ -925,6 +989,7 @@ constexpr int kWideTok = 64;                                      // tokens per 
 constexpr int kWideTiles = kWideTok / 32;                         // 32-token MFMA tiles
 constexpr uint32_t kWideSlotBytes = 4 * kWideTok * 16;            // 4 octets x tokens x 16 B
 static_assert(2 * kWideSlotBytes == kXWaveBytes, "wide ring slots must fill the dense ring");
+static_assert(kWideTok == kRecGroupTok, "a split record holds one wide matrix-core pass");
 
 template <int Q>
 struct WideStream {
@@ -1004,7 +1069,7 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
 }
 
 template <int Q>
-MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, f32x16 (&lo)[kWideTiles],
+MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, int ntiles, f32x16 (&lo)[kWideTiles],
                              f32x16 (&hi)[kWideTiles]) {
   constexpr int D = WideStream<Q>::D;
   for (int c0 = S.cb; c0 < S.ce; c0 += D) {
@@ -1032,6 +1097,7 @@ MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, f32x16 (&lo)[kWid
           const u32x4 va1 = {a1[0], a1[1], a1[2], a1[3]}, va2 = {a2[0], a2[1], a2[2], a2[3]};
 #pragma unroll
           for (int g = 0; g < kWideTiles; ++g) {
+            if (g >= ntiles) continue;   // a pass of at most 32 tokens fills one tile
             const u32x4 b = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (kWideTok * 16) + g * 512);
             lo[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va1),
                                                           __builtin_bit_cast(half8_t, b), lo[g], 0, 0, 0);
@@ -1133,7 +1199,7 @@ MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
     f32x16 lo[kWideTiles], hi[kWideTiles];
 #pragma unroll
     for (int g = 0; g < kWideTiles; ++g) lo[g] = hi[g] = f32x16{};
-    wide_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, lo, hi);
+    wide_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, (ng + 31) / 32, lo, hi);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the ring's last (re-read) loads
     const bool last = g0 + kWideTok >= it.n;
 #pragma unroll

@@ -53,7 +53,7 @@ constexpr int kRecTok = 4;   // tokens described in full (the streaming path's g
 // pass each), so that a hot expert's rows are spread over many workgroups instead of one
 // workgroup looping over its token groups.  Records of multi-token experts come first (their
 // items are the longest), then the streaming ones, each class in active-list order.
-constexpr int kRecGroupTok = 16;
+constexpr int kRecGroupTok = 64;
 constexpr int kRecSplitMaxPairs = 1024;
 inline size_t max_records(int T, int E, int k) {
   return static_cast<size_t>(E) + 2 + (static_cast<size_t>(T) * k + kRecGroupTok - 1) / kRecGroupTok;

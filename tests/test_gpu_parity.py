@@ -300,13 +300,14 @@ def test_layer_k1_and_k_equals_E():
     _check_layer(wl.TINY.replace(k=8, T=6, name="k=E"))
 
 
-@pytest.mark.parametrize("T", [70, 600], ids=["split-records", "whole-records"])
+@pytest.mark.parametrize("T", [70, 300, 600], ids=["one-pass", "split-records", "whole-records"])
 @pytest.mark.parametrize("threshold", [0, 1000], ids=["auto", "valu-max"])
 def test_layer_many_tokens_on_one_expert(threshold, T):
-    """More tokens per expert than one MFMA pass takes.  70 tokens x top-2 (140 pairs): each hot
-    expert's record is split into 16-token groups (the last one short enough for the VALU path
-    when it has at most 4 tokens); 600 tokens (1200 pairs, above the split limit): one record per
-    expert whose items loop over the 16-token groups."""
+    """More tokens per expert than one matrix-core pass takes.  70 tokens x top-2 over 4 experts
+    (about 35 per expert): one wide pass per item, second MFMA tile live.  300 tokens (600 pairs,
+    at most the split limit): each hot expert's record is split into 64-token groups, one wide
+    pass each, the last group ragged.  600 tokens (1200 pairs, above the split limit): one record
+    per expert whose items loop over 64-token passes."""
     shape = wl.TINY.replace(E=4, k=2, T=T, name="hot experts")
     _check_layer(shape, threshold=threshold)
 
