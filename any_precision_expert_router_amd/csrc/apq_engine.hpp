@@ -721,6 +721,7 @@ struct DenseStream {
   int cb, ce;
   u32x4 xrsrc;  // buffer resource of the activation rows (scalar registers)
   uint32_t rowoff[kDma];            // per lane: DMA i's byte offset (token lane%16, piece 4i + lane/16)
+  bool live;                        // per lane: its token is one of the pass's tokens
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, piece 0
 
@@ -731,7 +732,7 @@ struct DenseStream {
   MOE_INLINE void issue(int slot, int c) {
 #pragma unroll
     for (int i = 0; i < kDma; ++i)
-      lds_dma16(xring + slot * kXSlotBytes + i * 1024, rowoff[i], xrsrc, static_cast<uint32_t>(c) * 256u);
+      if (live) lds_dma16(xring + slot * kXSlotBytes + i * 1024, rowoff[i], xrsrc, static_cast<uint32_t>(c) * 256u);
 #pragma unroll
     for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u4 + static_cast<size_t>(c) * 64];
   }
@@ -813,17 +814,22 @@ MOE_INLINE void dense_chunk(const DenseStream<Q>& S, int s, uint32_t lane4, f32x
 
 template <int Q>
 MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& lo, f32x16& hi) {
-  constexpr int D = DenseStream<Q>::D;
-  for (int c0 = S.cb; c0 < S.ce; c0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const int c = c0 + s;
-      if (c < S.ce) {
-        dense_wait<Q>();
-        dense_chunk<Q>(S, s, lane4, lo, hi);
-        S.issue(s, S.clamp(c + D));
-      }
-    }
+  static_assert(DenseStream<Q>::D == 2, "the loop below walks the two ring slots in turn");
+  // Two chunks per iteration with every refill unconditional, so that the loads in flight at
+  // the loop head are the same on every path and the compiler's wait there keeps the ring full
+  // (a refill under a condition made it wait for every load, draining the ring each chunk).
+  int c = S.cb;
+  for (; c + 1 < S.ce; c += 2) {
+    dense_wait<Q>();
+    dense_chunk<Q>(S, 0, lane4, lo, hi);
+    S.issue(0, S.clamp(c + 2));
+    dense_wait<Q>();
+    dense_chunk<Q>(S, 1, lane4, lo, hi);
+    S.issue(1, S.clamp(c + 3));
+  }
+  if (c < S.ce) {
+    dense_wait<Q>();
+    dense_chunk<Q>(S, 0, lane4, lo, hi);
   }
 }
 
@@ -852,7 +858,7 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
     rows_total = A.T;
   }
   S.xrsrc = buffer_rsrc(base, static_cast<uint32_t>(rows_total * C * 2));
-  // token lane % 16 (tokens past ng re-read token g0's row; their columns are dropped)
+  // token lane % 16 (past ng: not staged; the row index only stays in range)
   const int t = lane & 15;
   const int tt = g0 + (t < ng ? t : 0);
   int row_index;
@@ -866,6 +872,9 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
   const uint32_t rb = static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) + (lane >> 4) * 16u;
 #pragma unroll
   for (int i = 0; i < DenseStream<Q>::kDma; ++i) S.rowoff[i] = rb + i * 64u;
+  // only live tokens are staged: a column of B past the pass's tokens holds whatever the slot
+  // held before, and the products of that column are never stored
+  S.live = t < ng;
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
   S.bx = S.xring + static_cast<uint32_t>(lane & 15) * 16u + static_cast<uint32_t>(lane >> 5) * 256u;
 }
@@ -1001,6 +1010,7 @@ struct WideStream {
   int cb, ce;                       // the item's chunks [cb, ce)
   u32x4 xrsrc;                      // buffer resource of the activation rows
   uint32_t rowoff;                  // per lane: byte offset of token (g0 + lane)'s word in row
+  bool live;                        // per lane: its token is one of the pass's tokens
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, octet 0, tile 0
 
@@ -1009,7 +1019,7 @@ struct WideStream {
   MOE_INLINE void issue(int slot, int c) {
 #pragma unroll
     for (int i = 0; i < kDma; ++i)
-      lds_dma16(xring + slot * kWideSlotBytes + i * (kWideTok * 16), rowoff + i * 16u, xrsrc,
+      if (live) lds_dma16(xring + slot * kWideSlotBytes + i * (kWideTok * 16), rowoff + i * 16u, xrsrc,
                 static_cast<uint32_t>(c) * 256u);
 #pragma unroll
     for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u32 + static_cast<size_t>(c) * 256];
@@ -1053,7 +1063,7 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
     rows_total = A.T;
   }
   S.xrsrc = buffer_rsrc(base, static_cast<uint32_t>(rows_total * C * 2));
-  // token lane (tokens past ng re-read token g0's row; their columns are dropped)
+  // token lane (past ng: not staged; the row index only stays in range)
   const int tt = g0 + (lane < ng ? lane : 0);
   int row_index;
   if constexpr (MODE == kGateUp) {
@@ -1064,50 +1074,71 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
     row_index = tt;
   }
   S.rowoff = static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) + static_cast<uint32_t>(wave) * 64u;
+  S.live = lane < ng;   // columns of tokens past ng are never stored (see the dense stream)
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
   S.bx = S.xring + static_cast<uint32_t>(lane >> 5) * (kWideTok * 16) + static_cast<uint32_t>(lane & 31) * 16u;
+}
+
+// One chunk of ring slot s: this wavefront's 32-column word of it for the pass's tokens.  The B
+// reads are issued ahead of the table lookups (LDS operations complete in order), and the
+// lookups together (see dense_lookup).
+template <int Q>
+MOE_INLINE void wide_chunk(const WideStream<Q>& S, int s, uint32_t lane4, int ntiles,
+                           f32x16 (&lo)[kWideTiles], f32x16 (&hi)[kWideTiles]) {
+  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kWideSlotBytes;
+  u32x4 b[2][kWideTiles];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int g = 0; g < kWideTiles; ++g)
+      if (g < ntiles) b[st][g] = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (kWideTok * 16) + g * 512);
+  uint32_t w[Q];
+#pragma unroll
+  for (int p = 0; p < Q; ++p) w[p] = S.buf[s][p];
+  uint32_t v[32];
+  dense_lookup<Q>(w, lane4, v);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t wv[16];
+  dense_finish<Q>(v, wv);
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    // k step st: octets 2 st and 2 st + 1 of the word (columns 16 st .. 16 st + 15)
+    uint32_t a1[4], a2[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(wv[8 * st + r], wv[8 * st + 4 + r], false, false);
+      a1[r] = sw[0];
+      a2[r] = sw[1];
+    }
+    const u32x4 va1 = {a1[0], a1[1], a1[2], a1[3]}, va2 = {a2[0], a2[1], a2[2], a2[3]};
+#pragma unroll
+    for (int g = 0; g < kWideTiles; ++g) {
+      if (g >= ntiles) continue;   // a pass of at most 32 tokens fills one tile
+      lo[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va1),
+                                                    __builtin_bit_cast(half8_t, b[st][g]), lo[g], 0, 0, 0);
+      hi[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va2),
+                                                    __builtin_bit_cast(half8_t, b[st][g]), hi[g], 0, 0, 0);
+    }
+  }
 }
 
 template <int Q>
 MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, int ntiles, f32x16 (&lo)[kWideTiles],
                              f32x16 (&hi)[kWideTiles]) {
-  constexpr int D = WideStream<Q>::D;
-  for (int c0 = S.cb; c0 < S.ce; c0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const int c = c0 + s;
-      if (c < S.ce) {
-        wide_wait<Q>();
-        uint32_t w[Q];
-#pragma unroll
-        for (int p = 0; p < Q; ++p) w[p] = S.buf[s][p];
-        uint32_t wv[16];
-        decode_word_dense<Q>(w, lane4, wv);
-        const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kWideSlotBytes;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          // k step st: octets 2 st and 2 st + 1 of the word (columns 16 st .. 16 st + 15)
-          uint32_t a1[4], a2[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(wv[8 * st + r], wv[8 * st + 4 + r], false, false);
-            a1[r] = sw[0];
-            a2[r] = sw[1];
-          }
-          const u32x4 va1 = {a1[0], a1[1], a1[2], a1[3]}, va2 = {a2[0], a2[1], a2[2], a2[3]};
-#pragma unroll
-          for (int g = 0; g < kWideTiles; ++g) {
-            if (g >= ntiles) continue;   // a pass of at most 32 tokens fills one tile
-            const u32x4 b = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (kWideTok * 16) + g * 512);
-            lo[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va1),
-                                                          __builtin_bit_cast(half8_t, b), lo[g], 0, 0, 0);
-            hi[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, va2),
-                                                          __builtin_bit_cast(half8_t, b), hi[g], 0, 0, 0);
-          }
-        }
-        S.issue(s, S.clamp(c + D));
-      }
-    }
+  static_assert(WideStream<Q>::D == 2, "the loop below walks the two ring slots in turn");
+  // two chunks per iteration, every refill unconditional (see dense_columns)
+  int c = S.cb;
+  for (; c + 1 < S.ce; c += 2) {
+    wide_wait<Q>();
+    wide_chunk<Q>(S, 0, lane4, ntiles, lo, hi);
+    S.issue(0, S.clamp(c + 2));
+    wide_wait<Q>();
+    wide_chunk<Q>(S, 1, lane4, ntiles, lo, hi);
+    S.issue(1, S.clamp(c + 3));
+  }
+  if (c < S.ce) {
+    wide_wait<Q>();
+    wide_chunk<Q>(S, 0, lane4, ntiles, lo, hi);
   }
 }
 
