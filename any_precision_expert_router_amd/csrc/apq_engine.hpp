@@ -43,6 +43,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // kernel, go through the scalar unit as constant-space loads.
 #define AS_GLOBAL __attribute__((address_space(1)))
 #define AS_CONST __attribute__((address_space(4)))
+#define AS_LDS __attribute__((address_space(3)))
 #define MOE_INLINE __device__ __attribute__((always_inline)) inline
 
 template <class T>
@@ -689,27 +690,16 @@ MOE_INLINE void decode_word_dense(const uint32_t (&w)[Q], uint32_t lane4, uint32
   dense_finish<Q>(v, wv);
 }
 
-// 16 bytes per lane from `rsrc` at voff + soff straight into LDS at m0 + 16 * lane.  The
-// compiler does not see this load, so it is counted by hand (dense_wait).  The lgkmcnt wait
-// makes sure the LDS reads of the slot's previous chunk have returned before it is refilled.
-// M0 is set here without the compiler's knowledge; the build checks that no compiler-generated
-// instruction of these kernels reads M0.
-MOE_INLINE void lds_dma16(uint32_t lds_addr, uint32_t voff, const u32x4& rsrc, uint32_t soff) {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory");
+// 16 bytes per lane from `src` straight into LDS at lds_addr + 16 * lane (a global load in its
+// LDS-DMA form).  The compiler sees it as a vector-memory load, so its own waits for later-used
+// registers count it; what it does not model is the LDS write, so readers of the staged bytes
+// wait by hand (dense_wait / wide_wait) and a slot is refilled only after an lgkmcnt(0).
+MOE_INLINE void lds_dma16(uint32_t lds_addr, const AS_GLOBAL char* src) {
+  __builtin_amdgcn_global_load_lds(src, (AS_LDS void*)(static_cast<uintptr_t>(lds_addr)), 16, 0, 0);
 }
 
-// Buffer resource of `bytes` bytes at `base` (raw buffer, no stride), as four wave-uniform
-// dwords, each read from the first lane, so that the asm's scalar operand is always in SGPRs
-// whatever the register pressure around it.
-MOE_INLINE u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4{static_cast<uint32_t>(uniform(static_cast<int>(a & 0xffffffffu))),
-               static_cast<uint32_t>(uniform(static_cast<int>((a >> 32) & 0xffffu))),
-               static_cast<uint32_t>(uniform(static_cast<int>(bytes))), 0x00020000u};
-}
+// The LDS reads of a ring slot's previous chunk have returned (it is about to be refilled).
+MOE_INLINE void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 template <int Q>
 struct DenseStream {
@@ -719,22 +709,29 @@ struct DenseStream {
   const AS_GLOBAL u32x4* pbase;
   size_t plane_u4;
   int cb, ce;
-  u32x4 xrsrc;  // buffer resource of the activation rows (scalar registers)
-  uint32_t rowoff[kDma];            // per lane: DMA i's byte offset (token lane%16, piece 4i + lane/16)
-  bool live;                        // per lane: its token is one of the pass's tokens
+  const AS_GLOBAL char* xsrc;       // per lane: DMA 0's source in chunk 0 (token lane%16, piece lane/16)
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, piece 0
 
   // Loads are issued unconditionally (a chunk past the end re-reads the last one, a cache hit)
   // so that the number of loads in flight is always the same.
   MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
-  // Activations of chunk c into slot `slot`, then its planes.
-  MOE_INLINE void issue(int slot, int c) {
-#pragma unroll
-    for (int i = 0; i < kDma; ++i)
-      if (live) lds_dma16(xring + slot * kXSlotBytes + i * 1024, rowoff[i], xrsrc, static_cast<uint32_t>(c) * 256u);
+  // The refill of slot `slot` with chunk c: its Q plane loads (registers), then its kDma staged
+  // activation loads (LDS), on every path.  The plane loads may go out as soon as the slot's
+  // plane words are consumed; the staging waits until the slot's B reads have returned.
+  MOE_INLINE void issue_planes(int slot, int c) {
 #pragma unroll
     for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u4 + static_cast<size_t>(c) * 64];
+  }
+  MOE_INLINE void issue_stage(int slot, int c) {
+    lds_reads_done();
+#pragma unroll
+    for (int i = 0; i < kDma; ++i)
+      lds_dma16(xring + slot * kXSlotBytes + i * 1024, xsrc + i * 64 + static_cast<size_t>(c) * 256);
+  }
+  MOE_INLINE void issue(int slot, int c) {
+    issue_planes(slot, c);
+    issue_stage(slot, c);
   }
   MOE_INLINE void prologue() {
 #pragma unroll
@@ -742,11 +739,11 @@ struct DenseStream {
   }
 };
 
-// The staged activations of the chunk about to be consumed have landed: after them were issued
-// its own planes, the next chunk's activations and the next chunk's planes.
+// The chunk about to be consumed has landed (its staged activations and its planes): only the
+// next chunk's kDma + Q loads may still be in flight.
 template <int Q>
 MOE_INLINE void dense_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * Q + DenseStream<Q>::kDma) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q + DenseStream<Q>::kDma) : "memory");
 }
 
 // A word's operands in flight: its two B operands (the staged activations of octets 4 JW ..
@@ -792,9 +789,12 @@ MOE_INLINE void dense_word_mma(const DenseWordOps<Q>& o, f32x16& lo, f32x16& hi)
 }
 
 // The four words of ring slot s, software-pipelined: word j + 1's lookups are issued before
-// word j's products, so the LDS latency overlaps the previous word's matrix-core work.
+// word j's products, so the LDS latency overlaps the previous word's matrix-core work.  Once the
+// last word's lookups and B reads are issued, the slot's registers and staged bytes are no
+// longer needed: its refill with chunk `next` goes out there, before the last two words'
+// products, which gives the refill that much more time to land.
 template <int Q>
-MOE_INLINE void dense_chunk(const DenseStream<Q>& S, int s, uint32_t lane4, f32x16& lo, f32x16& hi) {
+MOE_INLINE void dense_chunk(DenseStream<Q>& S, int s, int next, uint32_t lane4, f32x16& lo, f32x16& hi) {
   DenseWordOps<Q> a, b;
   dense_word_lookup<Q, 0>(S, s, lane4, a);
   dense_word_lookup<Q, 1>(S, s, lane4, b);
@@ -807,9 +807,12 @@ MOE_INLINE void dense_chunk(const DenseStream<Q>& S, int s, uint32_t lane4, f32x
   __builtin_amdgcn_sched_barrier(0);
   dense_word_lookup<Q, 3>(S, s, lane4, b);
   __builtin_amdgcn_sched_barrier(0);
+  if (next >= 0) S.issue_planes(s, next);
+  __builtin_amdgcn_sched_barrier(0);
   dense_word_mma<Q>(a, lo, hi);
   __builtin_amdgcn_sched_barrier(0);
   dense_word_mma<Q>(b, lo, hi);
+  if (next >= 0) S.issue_stage(s, next);
 }
 
 template <int Q>
@@ -821,15 +824,13 @@ MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& lo, f32
   int c = S.cb;
   for (; c + 1 < S.ce; c += 2) {
     dense_wait<Q>();
-    dense_chunk<Q>(S, 0, lane4, lo, hi);
-    S.issue(0, S.clamp(c + 2));
+    dense_chunk<Q>(S, 0, S.clamp(c + 2), lane4, lo, hi);
     dense_wait<Q>();
-    dense_chunk<Q>(S, 1, lane4, lo, hi);
-    S.issue(1, S.clamp(c + 3));
+    dense_chunk<Q>(S, 1, S.clamp(c + 3), lane4, lo, hi);
   }
   if (c < S.ce) {
     dense_wait<Q>();
-    dense_chunk<Q>(S, 0, lane4, lo, hi);
+    dense_chunk<Q>(S, 0, -1, lane4, lo, hi);
   }
 }
 
@@ -845,20 +846,13 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
   S.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
   S.cb = uniform(it.c0 + (it.nc * wave) / kWavesPerTile);
   S.ce = uniform(it.c0 + (it.nc * (wave + 1)) / kWavesPerTile);
-  const uint16_t* base;
-  size_t rows_total;
-  if constexpr (MODE == kGateUp) {
-    base = A.x;
-    rows_total = A.T;
-  } else if constexpr (MODE == kDown) {
+  const uint16_t* base;   // the activation rows: x (gate_up, plain) or act (down)
+  if constexpr (MODE == kDown) {
     base = it.shared ? A.act_shared : A.act;
-    rows_total = it.shared ? static_cast<size_t>(A.T) : static_cast<size_t>(A.T) * A.k;
   } else {
     base = A.x;
-    rows_total = A.T;
   }
-  S.xrsrc = buffer_rsrc(base, static_cast<uint32_t>(rows_total * C * 2));
-  // token lane % 16 (past ng: not staged; the row index only stays in range)
+  // token lane % 16 (tokens past ng re-read token g0's row: their columns are never stored)
   const int t = lane & 15;
   const int tt = g0 + (t < ng ? t : 0);
   int row_index;
@@ -869,12 +863,7 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
   } else {
     row_index = tt;
   }
-  const uint32_t rb = static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) + (lane >> 4) * 16u;
-#pragma unroll
-  for (int i = 0; i < DenseStream<Q>::kDma; ++i) S.rowoff[i] = rb + i * 64u;
-  // only live tokens are staged: a column of B past the pass's tokens holds whatever the slot
-  // held before, and the products of that column are never stored
-  S.live = t < ng;
+  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + (lane >> 4) * 16;
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
   S.bx = S.xring + static_cast<uint32_t>(lane & 15) * 16u + static_cast<uint32_t>(lane >> 5) * 256u;
 }
@@ -994,35 +983,44 @@ MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) 
 // sums over its quarter of the columns; they are reduced across wavefronts in LDS, one 32-token
 // tile at a time, through the drained rings.
 // ---------------------------------------------------------------------------------------------
-constexpr int kWideTok = 64;                                      // tokens per pass
-constexpr int kWideTiles = kWideTok / 32;                         // 32-token MFMA tiles
-constexpr uint32_t kWideSlotBytes = 4 * kWideTok * 16;            // 4 octets x tokens x 16 B
-static_assert(2 * kWideSlotBytes == kXWaveBytes, "wide ring slots must fill the dense ring");
+// A pass holds WT = 64 tokens, or 32 when the item has at most 32: the staging of a pass then
+// moves half the bytes with half the loads, and one MFMA tile serves it.
+constexpr int kWideTok = 64;                                      // tokens per full pass
+constexpr int kWideTiles = kWideTok / 32;                         // 32-token MFMA tiles (at most)
+template <int WT>
+constexpr uint32_t wide_slot_bytes() { return 4 * WT * 16; }      // 4 octets x tokens x 16 B
+static_assert(2 * wide_slot_bytes<kWideTok>() == kXWaveBytes, "wide ring slots must fill the dense ring");
 static_assert(kWideTok == kRecGroupTok, "a split record holds one wide matrix-core pass");
 
-template <int Q>
+template <int Q, int WT>
 struct WideStream {
   static constexpr int D = 2;       // chunks in flight per wavefront
-  static constexpr int kDma = 4;    // one LDS load per octet (64 lanes = 64 tokens)
+  // staged loads per chunk: 64 tokens, one per octet (lane = token); 32 tokens, one per two
+  // octets (lanes 0-31: octet 2i of token lane, lanes 32-63: octet 2i + 1 of token lane - 32)
+  static constexpr int kDma = WT / 16;
   uint32_t buf[D][Q];               // this wavefront's plane word of the chunk, per plane
   const AS_GLOBAL uint32_t* pbase;  // the lane's word in chunk 0 of plane 0
   size_t plane_u32;                 // plane stride in 32-bit words
   int cb, ce;                       // the item's chunks [cb, ce)
-  u32x4 xrsrc;                      // buffer resource of the activation rows
-  uint32_t rowoff;                  // per lane: byte offset of token (g0 + lane)'s word in row
-  bool live;                        // per lane: its token is one of the pass's tokens
+  const AS_GLOBAL char* xsrc;       // per lane: its token's first staged octet of chunk 0
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, octet 0, tile 0
 
   MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
-  // Activations of chunk c into slot `slot`, then its planes (loads issued unconditionally).
-  MOE_INLINE void issue(int slot, int c) {
-#pragma unroll
-    for (int i = 0; i < kDma; ++i)
-      if (live) lds_dma16(xring + slot * kWideSlotBytes + i * (kWideTok * 16), rowoff + i * 16u, xrsrc,
-                static_cast<uint32_t>(c) * 256u);
+  // The refill of slot `slot` with chunk c (see DenseStream).
+  MOE_INLINE void issue_planes(int slot, int c) {
 #pragma unroll
     for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u32 + static_cast<size_t>(c) * 256];
+  }
+  MOE_INLINE void issue_stage(int slot, int c) {
+    lds_reads_done();
+#pragma unroll
+    for (int i = 0; i < kDma; ++i)
+      lds_dma16(xring + slot * wide_slot_bytes<WT>() + i * 1024, xsrc + i * (WT == 64 ? 16 : 32) + static_cast<size_t>(c) * 256);
+  }
+  MOE_INLINE void issue(int slot, int c) {
+    issue_planes(slot, c);
+    issue_stage(slot, c);
   }
   MOE_INLINE void prologue() {
 #pragma unroll
@@ -1030,16 +1028,16 @@ struct WideStream {
   }
 };
 
-// The staged activations of the chunk about to be consumed have landed: after them were issued
-// its own planes, the next chunk's activations and the next chunk's planes.
-template <int Q>
+// The chunk about to be consumed has landed: only the next chunk's kDma + Q loads may still be
+// in flight.
+template <int Q, int WT>
 MOE_INLINE void wide_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * Q + WideStream<Q>::kDma) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q + WideStream<Q, WT>::kDma) : "memory");
 }
 
 // Geometry of the item for this wavefront and the activation rows of tokens [g0, g0 + ng).
-template <int MODE, int Q>
-MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng, WideStream<Q>& S) {
+template <int MODE, int Q, int WT>
+MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng, WideStream<Q, WT>& S) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int C = it.cols;
@@ -1050,21 +1048,15 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
   S.plane_u32 = static_cast<size_t>(it.rows) * C / 32;
   S.cb = it.c0;
   S.ce = it.c0 + it.nc;
-  const uint16_t* base;
-  size_t rows_total;
-  if constexpr (MODE == kGateUp) {
-    base = A.x;
-    rows_total = A.T;
-  } else if constexpr (MODE == kDown) {
+  const uint16_t* base;   // the activation rows: x (gate_up, plain) or act (down)
+  if constexpr (MODE == kDown) {
     base = it.shared ? A.act_shared : A.act;
-    rows_total = it.shared ? static_cast<size_t>(A.T) : static_cast<size_t>(A.T) * A.k;
   } else {
     base = A.x;
-    rows_total = A.T;
   }
-  S.xrsrc = buffer_rsrc(base, static_cast<uint32_t>(rows_total * C * 2));
-  // token lane (past ng: not staged; the row index only stays in range)
-  const int tt = g0 + (lane < ng ? lane : 0);
+  // the lane's token (tokens past ng re-read token g0's row: their columns are never stored)
+  const int t = WT == 64 ? lane : (lane & 31);
+  const int tt = g0 + (t < ng ? t : 0);
   int row_index;
   if constexpr (MODE == kGateUp) {
     row_index = it.shared ? tt : A.pairs[it.src_base + tt] / A.k;
@@ -1073,30 +1065,31 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
   } else {
     row_index = tt;
   }
-  S.rowoff = static_cast<uint32_t>(static_cast<size_t>(row_index) * C * 2) + static_cast<uint32_t>(wave) * 64u;
-  S.live = lane < ng;   // columns of tokens past ng are never stored (see the dense stream)
+  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + wave * 64 + (WT == 64 ? 0 : (lane >> 5) * 16);
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
-  S.bx = S.xring + static_cast<uint32_t>(lane >> 5) * (kWideTok * 16) + static_cast<uint32_t>(lane & 31) * 16u;
+  S.bx = S.xring + static_cast<uint32_t>(lane >> 5) * (WT * 16) + static_cast<uint32_t>(lane & 31) * 16u;
 }
 
 // One chunk of ring slot s: this wavefront's 32-column word of it for the pass's tokens.  The B
 // reads are issued ahead of the table lookups (LDS operations complete in order), and the
 // lookups together (see dense_lookup).
-template <int Q>
-MOE_INLINE void wide_chunk(const WideStream<Q>& S, int s, uint32_t lane4, int ntiles,
+template <int Q, int WT>
+MOE_INLINE void wide_chunk(WideStream<Q, WT>& S, int s, int next, uint32_t lane4, int ntiles,
                            f32x16 (&lo)[kWideTiles], f32x16 (&hi)[kWideTiles]) {
-  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kWideSlotBytes;
+  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * wide_slot_bytes<WT>();
   u32x4 b[2][kWideTiles];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int g = 0; g < kWideTiles; ++g)
-      if (g < ntiles) b[st][g] = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (kWideTok * 16) + g * 512);
+      if (g < ntiles) b[st][g] = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (WT * 16) + g * 512);
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = S.buf[s][p];
   uint32_t v[32];
   dense_lookup<Q>(w, lane4, v);
+  __builtin_amdgcn_sched_barrier(0);
+  if (next >= 0) S.issue_planes(s, next);   // the slot's plane words are consumed
   __builtin_amdgcn_sched_barrier(0);
   uint32_t wv[16];
   dense_finish<Q>(v, wv);
@@ -1120,25 +1113,24 @@ MOE_INLINE void wide_chunk(const WideStream<Q>& S, int s, uint32_t lane4, int nt
                                                     __builtin_bit_cast(half8_t, b[st][g]), hi[g], 0, 0, 0);
     }
   }
+  if (next >= 0) S.issue_stage(s, next);
 }
 
-template <int Q>
-MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, int ntiles, f32x16 (&lo)[kWideTiles],
+template <int Q, int WT>
+MOE_INLINE void wide_columns(WideStream<Q, WT>& S, uint32_t lane4, int ntiles, f32x16 (&lo)[kWideTiles],
                              f32x16 (&hi)[kWideTiles]) {
-  static_assert(WideStream<Q>::D == 2, "the loop below walks the two ring slots in turn");
+  static_assert(WideStream<Q, WT>::D == 2, "the loop below walks the two ring slots in turn");
   // two chunks per iteration, every refill unconditional (see dense_columns)
   int c = S.cb;
   for (; c + 1 < S.ce; c += 2) {
-    wide_wait<Q>();
-    wide_chunk<Q>(S, 0, lane4, ntiles, lo, hi);
-    S.issue(0, S.clamp(c + 2));
-    wide_wait<Q>();
-    wide_chunk<Q>(S, 1, lane4, ntiles, lo, hi);
-    S.issue(1, S.clamp(c + 3));
+    wide_wait<Q, WT>();
+    wide_chunk<Q, WT>(S, 0, S.clamp(c + 2), lane4, ntiles, lo, hi);
+    wide_wait<Q, WT>();
+    wide_chunk<Q, WT>(S, 1, S.clamp(c + 3), lane4, ntiles, lo, hi);
   }
   if (c < S.ce) {
-    wide_wait<Q>();
-    wide_chunk<Q>(S, 0, lane4, ntiles, lo, hi);
+    wide_wait<Q, WT>();
+    wide_chunk<Q, WT>(S, 0, -1, lane4, ntiles, lo, hi);
   }
 }
 
@@ -1210,29 +1202,29 @@ MOE_INLINE void wide_reduce_tile(const KArgs& A, const Item& it, int g0, int ng,
   __syncthreads();
 }
 
-template <int MODE, int Q>
+template <int MODE, int Q, int WT>
 MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   u32x4 L[kLutRegs];
   prefetch_lut_q<Q>(it, lane, wave, L);
-  WideStream<Q> S;
-  make_wide_stream<MODE, Q>(A, it, 0, min(kWideTok, it.n), S);
+  WideStream<Q, WT> S;
+  make_wide_stream<MODE, Q, WT>(A, it, 0, min(WT, it.n), S);
   S.prologue();
   write_dense_table<Q>(L, lane, wave);
   __syncthreads();
-  for (int g0 = 0; g0 < it.n; g0 += kWideTok) {
-    const int ng = min(kWideTok, it.n - g0);
+  for (int g0 = 0; g0 < it.n; g0 += WT) {
+    const int ng = min(WT, it.n - g0);
     if (g0 > 0) {
-      make_wide_stream<MODE, Q>(A, it, g0, ng, S);
+      make_wide_stream<MODE, Q, WT>(A, it, g0, ng, S);
       S.prologue();
     }
     f32x16 lo[kWideTiles], hi[kWideTiles];
 #pragma unroll
     for (int g = 0; g < kWideTiles; ++g) lo[g] = hi[g] = f32x16{};
-    wide_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, (ng + 31) / 32, lo, hi);
+    wide_columns<Q, WT>(S, static_cast<uint32_t>(lane) * 4u, (ng + 31) / 32, lo, hi);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the ring's last (re-read) loads
-    const bool last = g0 + kWideTok >= it.n;
+    const bool last = g0 + WT >= it.n;
 #pragma unroll
     for (int g = 0; g < kWideTiles; ++g)
       if (32 * g < ng) wide_reduce_tile<MODE>(A, it, g0, ng, g, lo[g], hi[g], last && g == 0 ? &Qu : nullptr);
@@ -1243,7 +1235,8 @@ MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
 // matrix-core path, wide when one 16-token pass would not hold its tokens.
 template <int MODE, int Q>
 MOE_INLINE void run_item(const KArgs& A, const Item& it, const Queue& Qu) {
-  if (it.n > kDenseGroup) run_item_wide<MODE, Q>(A, it, Qu);
+  if (it.n > 2 * kDenseGroup) run_item_wide<MODE, Q, kWideTok>(A, it, Qu);
+  else if (it.n > kDenseGroup) run_item_wide<MODE, Q, 32>(A, it, Qu);
   else run_item_dense<MODE, Q>(A, it, Qu);
 }
 

@@ -84,9 +84,6 @@ def _check_isa(tmp: str) -> None:
         flat = isa_check.flat_accesses(path)
         if flat:
             raise RuntimeError(f"flat memory instructions in {os.path.basename(path)}: {flat[:5]}")
-        m0 = isa_check.m0_foreign_uses(path)
-        if m0:
-            raise RuntimeError(f"M0 is used by compiler-generated code in {os.path.basename(path)}: {m0[:5]}")
     if total == 0:
         raise RuntimeError("no DPP instructions found in the device assembly: ISA check did not run")
 

@@ -16,10 +16,6 @@ and branches into its block) and reports each gap that is too short.
 `flat_accesses` reports flat (generic address) memory instructions.  A flat load may go to LDS or
 to global memory, so its result needs a wait for every vector load in flight (vmcnt(0)), which
 drains the streaming ring; every access in these kernels must name its address space.
-
-`m0_foreign_uses` reports instructions other than "s_mov_b32 m0, ..." that name M0: the
-hand-written buffer-to-LDS loads set M0 without telling the compiler, which is only safe while
-nothing else in the kernel reads it.
 """
 from __future__ import annotations
 
@@ -180,14 +176,6 @@ def scratch_users(path: str):
 
 def flat_accesses(path: str):
     return [t for kind, t in _program(path) if kind == "inst" and t.startswith("flat_")]
-
-
-def m0_foreign_uses(path: str):
-    out = []
-    for kind, t in _program(path):
-        if kind == "inst" and re.search(r"\bm0\b", t) and not t.startswith("s_mov_b32 m0,"):
-            out.append(t)
-    return out
 
 
 if __name__ == "__main__":

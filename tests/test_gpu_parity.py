@@ -188,12 +188,14 @@ def test_gemv_matches_oracle(q, T, dense, C):
 
 
 @pytest.mark.parametrize("q", range(1, 9))
-@pytest.mark.parametrize("T", [33, 64, 65, 130])
+@pytest.mark.parametrize("T", [17, 32, 33, 64, 65, 130])
 def test_gemv_wide_passes_match_oracle(q, T):
-    """More tokens than one 16-token matrix-core pass: the wide path (64 tokens per decode of the
-    weights, 32-token MFMA tiles, one 32-column word of each chunk per wavefront).  Token counts
-    cover one partly used tile, exactly one pass, one token into a second pass and a ragged third
-    pass; C = 2176 gives 17 chunks (an odd count for the two-slot ring)."""
+    """More tokens than one 16-token matrix-core pass: the wide path (one decode of the weights per
+    pass, 32-token MFMA tiles, one 32-column word of each chunk per wavefront).  17 and 32 tokens
+    take the 32-token pass (two staged loads per chunk, one tile); more take 64-token passes.
+    Token counts cover a barely used and a full 32-token pass, one partly used tile of a 64-token
+    pass, exactly one pass, one token into a second pass and a ragged third pass; C = 2176 gives 17
+    chunks (an odd count for the two-slot ring)."""
     say(f"gemv wide q={q} T={T}")
     R, C = 128, 2176
     r = np.random.default_rng(q * 1000 + T)
