@@ -35,6 +35,7 @@ namespace apq {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -134,6 +135,7 @@ MOE_INLINE int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 MOE_INLINE uint32_t word_of(const u32x4& v, int jw) {
   return jw == 0 ? v.x : jw == 1 ? v.y : jw == 2 ? v.z : v.w;
 }
+MOE_INLINE uint32_t word_of(const u32x2& v, int jw) { return jw == 0 ? v.x : v.y; }
 
 constexpr int kLutRegs = 8;  // 16-byte LUT registers one thread prefetches for an item
 
@@ -701,33 +703,62 @@ MOE_INLINE void lds_dma16(uint32_t lds_addr, const AS_GLOBAL char* src) {
 // The LDS reads of a ring slot's previous chunk have returned (it is about to be refilled).
 MOE_INLINE void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
-template <int Q>
+// A dense pass holds NT = 16 or 32 tokens.  Its chunk is 128 columns (a lane's 16-byte plane
+// unit, 4 words) for 16 tokens and 64 columns (half a unit, 2 words) for 32 tokens, so that a
+// staged chunk is 4 KiB either way: [8-column pieces][NT tokens][16 bytes].
+template <int NT>
+struct PlaneUnit;
+template <>
+struct PlaneUnit<16> {
+  typedef u32x4 type;
+  static constexpr int kWords = 4;
+};
+template <>
+struct PlaneUnit<32> {
+  typedef u32x2 type;
+  static constexpr int kWords = 2;
+};
+
+template <int Q, int NT>
 struct DenseStream {
   static constexpr int D = 2;       // chunks in flight per wavefront
-  static constexpr int kDma = 4;    // LDS loads per staged chunk (4 column pieces x 16 tokens)
-  u32x4 buf[D][Q];                  // plane units of a chunk
-  const AS_GLOBAL u32x4* pbase;
-  size_t plane_u4;
-  int cb, ce;
-  const AS_GLOBAL char* xsrc;       // per lane: DMA 0's source in chunk 0 (token lane%16, piece lane/16)
+  static constexpr int kDma = 4;    // LDS loads per staged chunk (4 KiB)
+  static constexpr int kWords = PlaneUnit<NT>::kWords;   // 32-column words per chunk
+  static constexpr uint32_t kPieceBytes = NT * 16;       // one 8-column piece of every token
+  typedef typename PlaneUnit<NT>::type unit_t;
+  unit_t buf[D][Q];                 // plane words of a chunk
+  const AS_GLOBAL unit_t* pbase;    // the lane's unit of chunk 0 of plane 0
+  size_t plane_units;               // plane stride in units
+  int cb, ce;                       // this wavefront's chunks [cb, ce)
+  const AS_GLOBAL char* xsrc;       // per lane: DMA 0's source in chunk 0
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, piece 0
 
   // Loads are issued unconditionally (a chunk past the end re-reads the last one, a cache hit)
   // so that the number of loads in flight is always the same.
   MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
+  MOE_INLINE const AS_GLOBAL unit_t* unit_of(int c) const {
+    if constexpr (NT == 16) {
+      return pbase + static_cast<size_t>(c) * 64;
+    } else {   // 64-column chunk c: half c & 1 of 16-byte unit c >> 1
+      return pbase + static_cast<size_t>(c >> 1) * 128 + (c & 1);
+    }
+  }
   // The refill of slot `slot` with chunk c: its Q plane loads (registers), then its kDma staged
   // activation loads (LDS), on every path.  The plane loads may go out as soon as the slot's
   // plane words are consumed; the staging waits until the slot's B reads have returned.
   MOE_INLINE void issue_planes(int slot, int c) {
+    const AS_GLOBAL unit_t* u = unit_of(c);
 #pragma unroll
-    for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u4 + static_cast<size_t>(c) * 64];
+    for (int p = 0; p < Q; ++p) buf[slot][p] = u[p * plane_units];
   }
   MOE_INLINE void issue_stage(int slot, int c) {
     lds_reads_done();
+    constexpr int kDmaStep = 4 * 16 * 16 / NT;                 // bytes of a token row per DMA
+    constexpr int kChunkBytes = kWords * 32 * 2;               // bytes of a token row per chunk
 #pragma unroll
     for (int i = 0; i < kDma; ++i)
-      lds_dma16(xring + slot * kXSlotBytes + i * 1024, xsrc + i * 64 + static_cast<size_t>(c) * 256);
+      lds_dma16(xring + slot * kXSlotBytes + i * 1024, xsrc + i * kDmaStep + static_cast<size_t>(c) * kChunkBytes);
   }
   MOE_INLINE void issue(int slot, int c) {
     issue_planes(slot, c);
@@ -741,9 +772,9 @@ struct DenseStream {
 
 // The chunk about to be consumed has landed (its staged activations and its planes): only the
 // next chunk's kDma + Q loads may still be in flight.
-template <int Q>
+template <int Q, int NT>
 MOE_INLINE void dense_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q + DenseStream<Q>::kDma) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q + DenseStream<Q, NT>::kDma) : "memory");
 }
 
 // A word's operands in flight: its two B operands (the staged activations of octets 4 JW ..
@@ -755,11 +786,12 @@ struct DenseWordOps {
   uint32_t v[32];
 };
 
-template <int Q, int JW>
-MOE_INLINE void dense_word_lookup(const DenseStream<Q>& S, int s, uint32_t lane4, DenseWordOps<Q>& o) {
+template <int Q, int NT, int JW>
+MOE_INLINE void dense_word_lookup(const DenseStream<Q, NT>& S, int s, uint32_t lane4, DenseWordOps<Q>& o) {
   const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kXSlotBytes;
 #pragma unroll
-  for (int pr = 0; pr < 2; ++pr) o.b[pr] = *reinterpret_cast<const u32x4*>(xb + (JW * 4 + 2 * pr) * 256);
+  for (int pr = 0; pr < 2; ++pr)
+    o.b[pr] = *reinterpret_cast<const u32x4*>(xb + (JW * 4 + 2 * pr) * DenseStream<Q, NT>::kPieceBytes);
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = word_of(S.buf[s][p], JW);
@@ -793,67 +825,75 @@ MOE_INLINE void dense_word_mma(const DenseWordOps<Q>& o, f32x16& lo, f32x16& hi)
 // last word's lookups and B reads are issued, the slot's registers and staged bytes are no
 // longer needed: its refill with chunk `next` goes out there, before the last two words'
 // products, which gives the refill that much more time to land.
-template <int Q>
-MOE_INLINE void dense_chunk(DenseStream<Q>& S, int s, int next, uint32_t lane4, f32x16& lo, f32x16& hi) {
+template <int Q, int NT>
+MOE_INLINE void dense_chunk(DenseStream<Q, NT>& S, int s, int next, uint32_t lane4, f32x16& lo, f32x16& hi) {
   DenseWordOps<Q> a, b;
-  dense_word_lookup<Q, 0>(S, s, lane4, a);
-  dense_word_lookup<Q, 1>(S, s, lane4, b);
+  dense_word_lookup<Q, NT, 0>(S, s, lane4, a);
+  dense_word_lookup<Q, NT, 1>(S, s, lane4, b);
   __builtin_amdgcn_sched_barrier(0);
   dense_word_mma<Q>(a, lo, hi);
   __builtin_amdgcn_sched_barrier(0);
-  dense_word_lookup<Q, 2>(S, s, lane4, a);
-  __builtin_amdgcn_sched_barrier(0);
-  dense_word_mma<Q>(b, lo, hi);
-  __builtin_amdgcn_sched_barrier(0);
-  dense_word_lookup<Q, 3>(S, s, lane4, b);
-  __builtin_amdgcn_sched_barrier(0);
-  if (next >= 0) S.issue_planes(s, next);
-  __builtin_amdgcn_sched_barrier(0);
-  dense_word_mma<Q>(a, lo, hi);
-  __builtin_amdgcn_sched_barrier(0);
-  dense_word_mma<Q>(b, lo, hi);
+  if constexpr (DenseStream<Q, NT>::kWords == 4) {
+    dense_word_lookup<Q, NT, 2>(S, s, lane4, a);
+    __builtin_amdgcn_sched_barrier(0);
+    dense_word_mma<Q>(b, lo, hi);
+    __builtin_amdgcn_sched_barrier(0);
+    dense_word_lookup<Q, NT, 3>(S, s, lane4, b);
+    __builtin_amdgcn_sched_barrier(0);
+    if (next >= 0) S.issue_planes(s, next);
+    __builtin_amdgcn_sched_barrier(0);
+    dense_word_mma<Q>(a, lo, hi);
+    __builtin_amdgcn_sched_barrier(0);
+    dense_word_mma<Q>(b, lo, hi);
+  } else {
+    if (next >= 0) S.issue_planes(s, next);
+    __builtin_amdgcn_sched_barrier(0);
+    dense_word_mma<Q>(b, lo, hi);
+  }
   if (next >= 0) S.issue_stage(s, next);
 }
 
-template <int Q>
-MOE_INLINE void dense_columns(DenseStream<Q>& S, uint32_t lane4, f32x16& lo, f32x16& hi) {
-  static_assert(DenseStream<Q>::D == 2, "the loop below walks the two ring slots in turn");
+template <int Q, int NT>
+MOE_INLINE void dense_columns(DenseStream<Q, NT>& S, uint32_t lane4, f32x16& lo, f32x16& hi) {
+  static_assert(DenseStream<Q, NT>::D == 2, "the loop below walks the two ring slots in turn");
   // Two chunks per iteration with every refill unconditional, so that the loads in flight at
   // the loop head are the same on every path and the compiler's wait there keeps the ring full
   // (a refill under a condition made it wait for every load, draining the ring each chunk).
   int c = S.cb;
   for (; c + 1 < S.ce; c += 2) {
-    dense_wait<Q>();
-    dense_chunk<Q>(S, 0, S.clamp(c + 2), lane4, lo, hi);
-    dense_wait<Q>();
-    dense_chunk<Q>(S, 1, S.clamp(c + 3), lane4, lo, hi);
+    dense_wait<Q, NT>();
+    dense_chunk<Q, NT>(S, 0, S.clamp(c + 2), lane4, lo, hi);
+    dense_wait<Q, NT>();
+    dense_chunk<Q, NT>(S, 1, S.clamp(c + 3), lane4, lo, hi);
   }
   if (c < S.ce) {
-    dense_wait<Q>();
-    dense_chunk<Q>(S, 0, -1, lane4, lo, hi);
+    dense_wait<Q, NT>();
+    dense_chunk<Q, NT>(S, 0, -1, lane4, lo, hi);
   }
 }
 
 // Geometry of the tile for this wavefront and the activation rows of tokens [g0, g0 + ng).
-template <int MODE, int Q>
-MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng, DenseStream<Q>& S) {
+template <int MODE, int Q, int NT>
+MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng, DenseStream<Q, NT>& S) {
+  typedef typename DenseStream<Q, NT>::unit_t unit_t;
+  constexpr int kPer = 4 / DenseStream<Q, NT>::kWords;   // chunks per 128 columns
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int C = it.cols;
   const int row = lane_row(it, lane);
   const int nc4 = C / kColChunk;
-  S.pbase = gview<u32x4>(it.planes) + static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel);
-  S.plane_u4 = static_cast<size_t>(it.rows) * C / 128;
-  S.cb = uniform(it.c0 + (it.nc * wave) / kWavesPerTile);
-  S.ce = uniform(it.c0 + (it.nc * (wave + 1)) / kWavesPerTile);
+  S.pbase = gview<unit_t>(it.planes) + (static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel)) * kPer;
+  S.plane_units = static_cast<size_t>(it.rows) * C / (32 * DenseStream<Q, NT>::kWords);
+  S.cb = uniform(kPer * it.c0 + (kPer * it.nc * wave) / kWavesPerTile);
+  S.ce = uniform(kPer * it.c0 + (kPer * it.nc * (wave + 1)) / kWavesPerTile);
   const uint16_t* base;   // the activation rows: x (gate_up, plain) or act (down)
   if constexpr (MODE == kDown) {
     base = it.shared ? A.act_shared : A.act;
   } else {
     base = A.x;
   }
-  // token lane % 16 (tokens past ng re-read token g0's row: their columns are never stored)
-  const int t = lane & 15;
+  // token lane % NT (tokens past ng re-read token g0's row: their columns are never stored)
+  const int t = lane & (NT - 1);
   const int tt = g0 + (t < ng ? t : 0);
   int row_index;
   if constexpr (MODE == kGateUp) {
@@ -863,16 +903,17 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
   } else {
     row_index = tt;
   }
-  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + (lane >> 4) * 16;
+  // DMA lane l: token l % NT, piece l / NT of the DMA's group of 64 / NT pieces
+  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + (lane / NT) * 16;
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
-  S.bx = S.xring + static_cast<uint32_t>(lane & 15) * 16u + static_cast<uint32_t>(lane >> 5) * 256u;
+  S.bx = S.xring + static_cast<uint32_t>(lane & (NT - 1)) * 16u + static_cast<uint32_t>(lane >> 5) * DenseStream<Q, NT>::kPieceBytes;
 }
 
 // D layout of the 32x32 MFMA: lane l, register i holds D[m][l % 32] with
 // m = 8 (i / 4) + 4 (l / 32) + i % 4; `lo` covers tile rows m, `hi` rows 32 + m.  Columns
 // l % 32 < 16 are token l % 16 (the other 16 repeat them).  The partial sums of wavefronts 1-3
 // go through their own (drained) activation rings.
-template <int MODE>
+template <int MODE, int NT>
 MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, f32x16& lo,
                                        f32x16& hi, const Queue* Qu) {
   const int lane = threadIdx.x & 63;
@@ -899,8 +940,8 @@ MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, i
         hi[i] += other[(16 + i) * 64 + lane];
       }
     }
-    const int tok = lane & 15;
-    const bool live = (lane & 16) == 0 && tok < ng;
+    const int tok = lane & (NT - 1);
+    const bool live = (NT == 32 || (lane & 16) == 0) && tok < ng;
     // this lane's output row base and scale, computed once (rows r0 + m and r0 + 32 + m follow)
     uint16_t* act_dst = nullptr;
     float* out_dst = nullptr;
@@ -943,26 +984,26 @@ MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, i
   __syncthreads();
 }
 
-template <int MODE, int Q>
+template <int MODE, int Q, int NT>
 MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   u32x4 L[kLutRegs];
   prefetch_lut_q<Q>(it, lane, wave, L);
-  DenseStream<Q> S;
-  make_dense_stream<MODE, Q>(A, it, 0, min(kDenseGroup, it.n), S);
+  DenseStream<Q, NT> S;
+  make_dense_stream<MODE, Q, NT>(A, it, 0, min(NT, it.n), S);
   S.prologue();
   write_dense_table<Q>(L, lane, wave);
   __syncthreads();
-  for (int g0 = 0; g0 < it.n; g0 += kDenseGroup) {
-    const int ng = min(kDenseGroup, it.n - g0);
+  for (int g0 = 0; g0 < it.n; g0 += NT) {
+    const int ng = min(NT, it.n - g0);
     if (g0 > 0) {
-      make_dense_stream<MODE, Q>(A, it, g0, ng, S);
+      make_dense_stream<MODE, Q, NT>(A, it, g0, ng, S);
       S.prologue();
     }
     f32x16 lo = {}, hi = {};
-    dense_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, lo, hi);
-    dense_reduce_and_store<MODE>(A, it, g0, ng, lo, hi, g0 + kDenseGroup >= it.n ? &Qu : nullptr);
+    dense_columns<Q, NT>(S, static_cast<uint32_t>(lane) * 4u, lo, hi);
+    dense_reduce_and_store<MODE, NT>(A, it, g0, ng, lo, hi, g0 + NT >= it.n ? &Qu : nullptr);
   }
 }
 
@@ -1236,8 +1277,8 @@ MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
 template <int MODE, int Q>
 MOE_INLINE void run_item(const KArgs& A, const Item& it, const Queue& Qu) {
   if (it.n > 2 * kDenseGroup) run_item_wide<MODE, Q, kWideTok>(A, it, Qu);
-  else if (it.n > kDenseGroup) run_item_wide<MODE, Q, 32>(A, it, Qu);
-  else run_item_dense<MODE, Q>(A, it, Qu);
+  else if (it.n > kDenseGroup) run_item_dense<MODE, Q, 32>(A, it, Qu);
+  else run_item_dense<MODE, Q, 16>(A, it, Qu);
 }
 
 // ---------------------------------------------------------------------------------------------
