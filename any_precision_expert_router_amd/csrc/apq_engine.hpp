@@ -909,79 +909,112 @@ MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng
   S.bx = S.xring + static_cast<uint32_t>(lane & (NT - 1)) * 16u + static_cast<uint32_t>(lane >> 5) * DenseStream<Q, NT>::kPieceBytes;
 }
 
+// Where lane `lane`'s token of a matrix-core tile goes: the output row base and the scale
+// (rows r0 + m follow), or nothing when the lane's column is not a live token.
+struct TileOut {
+  uint16_t* act_dst;
+  float* out_dst;
+  float scale;
+  bool live;
+};
+
+template <int MODE>
+MOE_INLINE TileOut tile_out(const KArgs& A, const Item& it, int g0, int tok, bool live) {
+  TileOut o{nullptr, nullptr, 1.0f, live};
+  if (!live) return o;
+  if constexpr (MODE == kGateUp) {
+    o.act_dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + tok) * A.I_shared + it.r0
+                          : A.act + static_cast<size_t>(it.src_base + g0 + tok) * A.I + it.r0;
+  } else if constexpr (MODE == kDown) {
+    if (it.shared) {
+      if (A.shared_scale) o.scale = A.shared_scale[g0 + tok];
+      o.out_dst = A.part_shared + (static_cast<size_t>(it.seg) * A.T + g0 + tok) * A.H;
+    } else {
+      const int p = A.pairs[it.src_base + g0 + tok];
+      o.scale = A.gates[p];
+      o.out_dst = A.part + (static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H;
+    }
+    o.out_dst += it.r0;
+  } else {
+    o.out_dst = A.y_plain + static_cast<size_t>(g0 + tok) * it.rows + it.r0;
+  }
+  return o;
+}
+
+// Wavefront W's quarter of the reduction: registers i = 4W .. 4W + 3 of lo and hi (tile rows
+// m = 8W + 4 (lane / 32) + i % 4 and 32 + m), summed over the four wavefronts in the fixed order
+// 0 + 1 + 2 + 3 (its own values from registers, the others' from their rings), then stored.
+template <int MODE, int W>
+MOE_INLINE void reduce_quarter(const f32x16& lo, const f32x16& hi, const float* ring, int lane, const TileOut& o) {
+  float sl[4], sh[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * W + j;
+#pragma unroll
+    for (int w = 0; w < kWavesPerTile; ++w) {
+      const float* other = ring + w * (kXWaveBytes / 4);
+      const float a = w == W ? lo[i] : other[i * 64 + lane];
+      const float b = w == W ? hi[i] : other[(16 + i) * 64 + lane];
+      sl[j] = w == 0 ? a : sl[j] + a;
+      sh[j] = w == 0 ? b : sh[j] + b;
+    }
+  }
+  if (!o.live) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = 8 * W + 4 * (lane >> 5) + j;
+    if constexpr (MODE == kGateUp) {
+      // gate row r0 + m and up row row_hi + m meet in the same lane and register
+      o.act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(silu_mul(sl[j], sh[j])));
+    } else {
+      o.out_dst[m] = o.scale * sl[j];
+      o.out_dst[32 + m] = o.scale * sh[j];
+    }
+  }
+}
+
 // D layout of the 32x32 MFMA: lane l, register i holds D[m][l % 32] with
-// m = 8 (i / 4) + 4 (l / 32) + i % 4; `lo` covers tile rows m, `hi` rows 32 + m.  Columns
-// l % 32 < 16 are token l % 16 (the other 16 repeat them).  The partial sums of wavefronts 1-3
-// go through their own (drained) activation rings.
-template <int MODE, int NT>
-MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, f32x16& lo,
-                                       f32x16& hi, const Queue* Qu) {
+// m = 8 (i / 4) + 4 (l / 32) + i % 4; `lo` covers tile rows m, `hi` rows 32 + m.  The four
+// wavefronts hold partial sums over their own columns.  Each writes the 24 registers it does not
+// reduce into its own (drained) activation ring, and after one barrier each reduces and stores
+// a quarter of the tile's rows (registers 4W .. 4W + 3), so the reduction and the stores are
+// spread over the four wavefronts instead of serialised in one.
+template <int MODE>
+MOE_INLINE void reduce_tile(const KArgs& A, const Item& it, int g0, int tok, bool live, f32x16& lo,
+                            f32x16& hi, const Queue* Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the ring's last (re-read) loads
   float* ring = reinterpret_cast<float*>(reinterpret_cast<char*>(g_lds) + kXRingBase);
-  if (wave > 0) {
-    float* mine = ring + wave * (kXWaveBytes / 4);
+  float* mine = ring + wave * (kXWaveBytes / 4);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 16; ++i) {
+    if ((i >> 2) != wave) {
       mine[i * 64 + lane] = lo[i];
       mine[(16 + i) * 64 + lane] = hi[i];
     }
   }
   if (Qu) queue_publish(*Qu);
+  const TileOut o = tile_out<MODE>(A, it, g0, tok, live);
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 1; w < kWavesPerTile; ++w) {
-      const float* other = ring + w * (kXWaveBytes / 4);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        lo[i] += other[i * 64 + lane];
-        hi[i] += other[(16 + i) * 64 + lane];
-      }
-    }
-    const int tok = lane & (NT - 1);
-    const bool live = (NT == 32 || (lane & 16) == 0) && tok < ng;
-    // this lane's output row base and scale, computed once (rows r0 + m and r0 + 32 + m follow)
-    uint16_t* act_dst = nullptr;
-    float* out_dst = nullptr;
-    float scale = 1.0f;
-    if (live) {
-      if constexpr (MODE == kGateUp) {
-        act_dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + tok) * A.I_shared + it.r0
-                            : A.act + static_cast<size_t>(it.src_base + g0 + tok) * A.I + it.r0;
-      } else if constexpr (MODE == kDown) {
-        if (it.shared) {
-          if (A.shared_scale) scale = A.shared_scale[g0 + tok];
-          out_dst = A.part_shared + (static_cast<size_t>(it.seg) * A.T + g0 + tok) * A.H;
-        } else {
-          const int p = A.pairs[it.src_base + g0 + tok];
-          scale = A.gates[p];
-          out_dst = A.part + (static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H;
-        }
-        out_dst += it.r0;
-      } else {
-        out_dst = A.y_plain + static_cast<size_t>(g0 + tok) * it.rows + it.r0;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if constexpr (MODE == kGateUp) {
-        // gate row r0 + m and up row row_hi + m meet in the same lane and register
-        if (live) {
-          const float g = lo[i];
-          act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(silu_mul(g, hi[i])));
-        }
-      } else {
-        if (live) {
-          out_dst[m] = scale * lo[i];
-          out_dst[32 + m] = scale * hi[i];
-        }
-      }
-    }
+  switch (wave) {
+    case 0: reduce_quarter<MODE, 0>(lo, hi, ring, lane, o); break;
+    case 1: reduce_quarter<MODE, 1>(lo, hi, ring, lane, o); break;
+    case 2: reduce_quarter<MODE, 2>(lo, hi, ring, lane, o); break;
+    default: reduce_quarter<MODE, 3>(lo, hi, ring, lane, o); break;
   }
   __syncthreads();
+}
+
+// Columns l % 32 < 16 of a 16-token pass are token l % 16 (the other 16 repeat them); a 32-token
+// pass has token l % 32 in column l % 32.
+template <int MODE, int NT>
+MOE_INLINE void dense_reduce_and_store(const KArgs& A, const Item& it, int g0, int ng, f32x16& lo,
+                                       f32x16& hi, const Queue* Qu) {
+  const int lane = threadIdx.x & 63;
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the ring's last (re-read) loads
+  const int tok = lane & (NT - 1);
+  const bool live = (NT == 32 || (lane & 16) == 0) && tok < ng;
+  reduce_tile<MODE>(A, it, g0, tok, live, lo, hi, Qu);
 }
 
 template <int MODE, int Q, int NT>
@@ -1176,71 +1209,13 @@ MOE_INLINE void wide_columns(WideStream<Q, WT>& S, uint32_t lane4, int ntiles, f
 }
 
 // Reduce the four wavefronts' partial sums of one 32-token tile (tokens g0 + 32 g ..) and store
-// them.  D layout: lane l, register i holds row m = 8 (i / 4) + 4 (l / 32) + i % 4 of `lo`
-// (32 + m of `hi`) for token 32 g + l % 32.
+// them (reduce_tile).  D layout: lane l holds token 32 g + l % 32.
 template <int MODE>
 MOE_INLINE void wide_reduce_tile(const KArgs& A, const Item& it, int g0, int ng, int g, f32x16& lo,
                                  f32x16& hi, const Queue* Qu) {
   const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  float* ring = reinterpret_cast<float*>(reinterpret_cast<char*>(g_lds) + kXRingBase);
-  if (wave > 0) {
-    float* mine = ring + wave * (kXWaveBytes / 4);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mine[i * 64 + lane] = lo[i];
-      mine[(16 + i) * 64 + lane] = hi[i];
-    }
-  }
-  if (Qu) queue_publish(*Qu);
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int w = 1; w < kWavesPerTile; ++w) {
-      const float* other = ring + w * (kXWaveBytes / 4);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        lo[i] += other[i * 64 + lane];
-        hi[i] += other[(16 + i) * 64 + lane];
-      }
-    }
-    const int tok = 32 * g + (lane & 31);
-    const bool live = tok < ng;
-    uint16_t* act_dst = nullptr;
-    float* out_dst = nullptr;
-    float scale = 1.0f;
-    if (live) {
-      if constexpr (MODE == kGateUp) {
-        act_dst = it.shared ? A.act_shared + static_cast<size_t>(g0 + tok) * A.I_shared + it.r0
-                            : A.act + static_cast<size_t>(it.src_base + g0 + tok) * A.I + it.r0;
-      } else if constexpr (MODE == kDown) {
-        if (it.shared) {
-          if (A.shared_scale) scale = A.shared_scale[g0 + tok];
-          out_dst = A.part_shared + (static_cast<size_t>(it.seg) * A.T + g0 + tok) * A.H;
-        } else {
-          const int p = A.pairs[it.src_base + g0 + tok];
-          scale = A.gates[p];
-          out_dst = A.part + (static_cast<size_t>(it.seg) * A.T * A.k + p) * A.H;
-        }
-        out_dst += it.r0;
-      } else {
-        out_dst = A.y_plain + static_cast<size_t>(g0 + tok) * it.rows + it.r0;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if constexpr (MODE == kGateUp) {
-        if (live) act_dst[m] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(silu_mul(lo[i], hi[i])));
-      } else {
-        if (live) {
-          out_dst[m] = scale * lo[i];
-          out_dst[32 + m] = scale * hi[i];
-        }
-      }
-    }
-  }
-  __syncthreads();
+  const int tok = 32 * g + (lane & 31);
+  reduce_tile<MODE>(A, it, g0, tok, tok < ng, lo, hi, Qu);
 }
 
 template <int MODE, int Q, int WT>
