@@ -54,7 +54,7 @@ MOE_INLINE const AS_CONST T* cview(const void* p) { return (const AS_CONST T*)p;
 
 constexpr int kThreads = 64 * kWavesPerTile;
 constexpr int kMaxTokGroup = 4;                  // tokens sharing one VALU pass over the weights
-constexpr int kDenseGroup = 16;                  // tokens per MFMA pass (32x32 tile: 2 row halves x 16)
+constexpr int kDenseGroup = 16;                  // tokens of the smaller dense MFMA pass (32x32 tile)
 
 // LDS map of a tile workgroup (bytes):
 //   [0, 64K)        lookup tables, 4-byte slots [entry][64 lanes] unless noted.  Streaming (VALU)
@@ -62,10 +62,11 @@ constexpr int kDenseGroup = 16;                  // tokens per MFMA pass (32x32 
 //                   (q >= 5).  Dense (MFMA) tiles keep their table below 32K: the pair table for
 //                   q <= 3, the single table for q = 4..7, the single table with 2-byte slots
 //                   for q = 8.
-//   [32K, 64K)      dense tiles only: each wavefront's 8K ring of two staged activation chunks,
-//                   [slot][16 column pieces][16 tokens][16 bytes] fp16, filled by buffer loads
-//                   straight to LDS; after the tile's columns it holds that wavefront's partial
-//                   sums for the cross-wavefront reduction.
+//   [32K, 64K)      matrix-core tiles only: each wavefront's 8K ring of two staged activation
+//                   chunks of 4K, [8-column pieces][tokens][16 bytes] fp16 (16 pieces x 16
+//                   tokens, 8 x 32, or for wide passes 4 x 64), filled by loads straight to LDS;
+//                   after the tile's columns it holds that wavefront's partial sums for the
+//                   cross-wavefront reduction.
 //   [64K, 67K)      streaming tiles: cross-wavefront reduction (4 floats per lane, waves 1-3).
 //   [67K, 67K+16)   the work queue's next item index.
 constexpr uint32_t kTblBytes = 65536;
@@ -1041,9 +1042,9 @@ MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Wide tiles (more tokens than one matrix-core group: prefill chunks, where an expert meets
-// hundreds of tokens).  The dense path above decodes the weights once per 16 tokens; here each
-// decode serves kWideTok tokens, so the decode work per token falls by kWideTok / 16.
+// Wide tiles (more tokens than one 32-token dense pass: prefill chunks, where an expert meets
+// hundreds of tokens).  The dense passes decode the weights once per 16 or 32 tokens; here each
+// decode serves kWideTok tokens.
 //
 // The four wavefronts take one 32-column word each of every 128-column chunk (wavefront w: word
 // w), so a wavefront needs the activations of its own 32 columns only: its LDS ring slot holds
@@ -1057,21 +1058,16 @@ MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) 
 // sums over its quarter of the columns; they are reduced across wavefronts in LDS, one 32-token
 // tile at a time, through the drained rings.
 // ---------------------------------------------------------------------------------------------
-// A pass holds WT = 64 tokens, or 32 when the item has at most 32: the staging of a pass then
-// moves half the bytes with half the loads, and one MFMA tile serves it.
-constexpr int kWideTok = 64;                                      // tokens per full pass
-constexpr int kWideTiles = kWideTok / 32;                         // 32-token MFMA tiles (at most)
-template <int WT>
-constexpr uint32_t wide_slot_bytes() { return 4 * WT * 16; }      // 4 octets x tokens x 16 B
-static_assert(2 * wide_slot_bytes<kWideTok>() == kXWaveBytes, "wide ring slots must fill the dense ring");
+constexpr int kWideTok = 64;                                      // tokens per pass
+constexpr int kWideTiles = kWideTok / 32;                         // 32-token MFMA tiles
+constexpr uint32_t kWideSlotBytes = 4 * kWideTok * 16;            // 4 octets x tokens x 16 B
+static_assert(2 * kWideSlotBytes == kXWaveBytes, "wide ring slots must fill the dense ring");
 static_assert(kWideTok == kRecGroupTok, "a split record holds one wide matrix-core pass");
 
-template <int Q, int WT>
+template <int Q>
 struct WideStream {
   static constexpr int D = 2;       // chunks in flight per wavefront
-  // staged loads per chunk: 64 tokens, one per octet (lane = token); 32 tokens, one per two
-  // octets (lanes 0-31: octet 2i of token lane, lanes 32-63: octet 2i + 1 of token lane - 32)
-  static constexpr int kDma = WT / 16;
+  static constexpr int kDma = 4;    // staged loads per chunk: one per octet (lane = token)
   uint32_t buf[D][Q];               // this wavefront's plane word of the chunk, per plane
   const AS_GLOBAL uint32_t* pbase;  // the lane's word in chunk 0 of plane 0
   size_t plane_u32;                 // plane stride in 32-bit words
@@ -1090,7 +1086,7 @@ struct WideStream {
     lds_reads_done();
 #pragma unroll
     for (int i = 0; i < kDma; ++i)
-      lds_dma16(xring + slot * wide_slot_bytes<WT>() + i * 1024, xsrc + i * (WT == 64 ? 16 : 32) + static_cast<size_t>(c) * 256);
+      lds_dma16(xring + slot * kWideSlotBytes + i * 1024, xsrc + i * 16 + static_cast<size_t>(c) * 256);
   }
   MOE_INLINE void issue(int slot, int c) {
     issue_planes(slot, c);
@@ -1104,14 +1100,14 @@ struct WideStream {
 
 // The chunk about to be consumed has landed: only the next chunk's kDma + Q loads may still be
 // in flight.
-template <int Q, int WT>
+template <int Q>
 MOE_INLINE void wide_wait() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q + WideStream<Q, WT>::kDma) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q + WideStream<Q>::kDma) : "memory");
 }
 
 // Geometry of the item for this wavefront and the activation rows of tokens [g0, g0 + ng).
-template <int MODE, int Q, int WT>
-MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng, WideStream<Q, WT>& S) {
+template <int MODE, int Q>
+MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng, WideStream<Q>& S) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int C = it.cols;
@@ -1129,7 +1125,7 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
     base = A.x;
   }
   // the lane's token (tokens past ng re-read token g0's row: their columns are never stored)
-  const int t = WT == 64 ? lane : (lane & 31);
+  const int t = lane;
   const int tt = g0 + (t < ng ? t : 0);
   int row_index;
   if constexpr (MODE == kGateUp) {
@@ -1139,24 +1135,24 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
   } else {
     row_index = tt;
   }
-  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + wave * 64 + (WT == 64 ? 0 : (lane >> 5) * 16);
+  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + wave * 64;
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
-  S.bx = S.xring + static_cast<uint32_t>(lane >> 5) * (WT * 16) + static_cast<uint32_t>(lane & 31) * 16u;
+  S.bx = S.xring + static_cast<uint32_t>(lane >> 5) * (kWideTok * 16) + static_cast<uint32_t>(lane & 31) * 16u;
 }
 
 // One chunk of ring slot s: this wavefront's 32-column word of it for the pass's tokens.  The B
 // reads are issued ahead of the table lookups (LDS operations complete in order), and the
 // lookups together (see dense_lookup).
-template <int Q, int WT>
-MOE_INLINE void wide_chunk(WideStream<Q, WT>& S, int s, int next, uint32_t lane4, int ntiles,
+template <int Q>
+MOE_INLINE void wide_chunk(WideStream<Q>& S, int s, int next, uint32_t lane4, int ntiles,
                            f32x16 (&lo)[kWideTiles], f32x16 (&hi)[kWideTiles]) {
-  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * wide_slot_bytes<WT>();
+  const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kWideSlotBytes;
   u32x4 b[2][kWideTiles];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int g = 0; g < kWideTiles; ++g)
-      if (g < ntiles) b[st][g] = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (WT * 16) + g * 512);
+      if (g < ntiles) b[st][g] = *reinterpret_cast<const u32x4*>(xb + (2 * st) * (kWideTok * 16) + g * 512);
   uint32_t w[Q];
 #pragma unroll
   for (int p = 0; p < Q; ++p) w[p] = S.buf[s][p];
@@ -1190,21 +1186,21 @@ MOE_INLINE void wide_chunk(WideStream<Q, WT>& S, int s, int next, uint32_t lane4
   if (next >= 0) S.issue_stage(s, next);
 }
 
-template <int Q, int WT>
-MOE_INLINE void wide_columns(WideStream<Q, WT>& S, uint32_t lane4, int ntiles, f32x16 (&lo)[kWideTiles],
+template <int Q>
+MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, int ntiles, f32x16 (&lo)[kWideTiles],
                              f32x16 (&hi)[kWideTiles]) {
-  static_assert(WideStream<Q, WT>::D == 2, "the loop below walks the two ring slots in turn");
+  static_assert(WideStream<Q>::D == 2, "the loop below walks the two ring slots in turn");
   // two chunks per iteration, every refill unconditional (see dense_columns)
   int c = S.cb;
   for (; c + 1 < S.ce; c += 2) {
-    wide_wait<Q, WT>();
-    wide_chunk<Q, WT>(S, 0, S.clamp(c + 2), lane4, ntiles, lo, hi);
-    wide_wait<Q, WT>();
-    wide_chunk<Q, WT>(S, 1, S.clamp(c + 3), lane4, ntiles, lo, hi);
+    wide_wait<Q>();
+    wide_chunk<Q>(S, 0, S.clamp(c + 2), lane4, ntiles, lo, hi);
+    wide_wait<Q>();
+    wide_chunk<Q>(S, 1, S.clamp(c + 3), lane4, ntiles, lo, hi);
   }
   if (c < S.ce) {
-    wide_wait<Q, WT>();
-    wide_chunk<Q, WT>(S, 0, -1, lane4, ntiles, lo, hi);
+    wide_wait<Q>();
+    wide_chunk<Q>(S, 0, -1, lane4, ntiles, lo, hi);
   }
 }
 
@@ -1218,29 +1214,29 @@ MOE_INLINE void wide_reduce_tile(const KArgs& A, const Item& it, int g0, int ng,
   reduce_tile<MODE>(A, it, g0, tok, tok < ng, lo, hi, Qu);
 }
 
-template <int MODE, int Q, int WT>
+template <int MODE, int Q>
 MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   u32x4 L[kLutRegs];
   prefetch_lut_q<Q>(it, lane, wave, L);
-  WideStream<Q, WT> S;
-  make_wide_stream<MODE, Q, WT>(A, it, 0, min(WT, it.n), S);
+  WideStream<Q> S;
+  make_wide_stream<MODE, Q>(A, it, 0, min(kWideTok, it.n), S);
   S.prologue();
   write_dense_table<Q>(L, lane, wave);
   __syncthreads();
-  for (int g0 = 0; g0 < it.n; g0 += WT) {
-    const int ng = min(WT, it.n - g0);
+  for (int g0 = 0; g0 < it.n; g0 += kWideTok) {
+    const int ng = min(kWideTok, it.n - g0);
     if (g0 > 0) {
-      make_wide_stream<MODE, Q, WT>(A, it, g0, ng, S);
+      make_wide_stream<MODE, Q>(A, it, g0, ng, S);
       S.prologue();
     }
     f32x16 lo[kWideTiles], hi[kWideTiles];
 #pragma unroll
     for (int g = 0; g < kWideTiles; ++g) lo[g] = hi[g] = f32x16{};
-    wide_columns<Q, WT>(S, static_cast<uint32_t>(lane) * 4u, (ng + 31) / 32, lo, hi);
+    wide_columns<Q>(S, static_cast<uint32_t>(lane) * 4u, (ng + 31) / 32, lo, hi);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");  // the ring's last (re-read) loads
-    const bool last = g0 + WT >= it.n;
+    const bool last = g0 + kWideTok >= it.n;
 #pragma unroll
     for (int g = 0; g < kWideTiles; ++g)
       if (32 * g < ng) wide_reduce_tile<MODE>(A, it, g0, ng, g, lo[g], hi[g], last && g == 0 ? &Qu : nullptr);
@@ -1248,10 +1244,10 @@ MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
 }
 
 // A tile that does not stream (at least as many tokens as the dense threshold, or more than 4):
-// matrix-core path, wide when one 16-token pass would not hold its tokens.
+// matrix-core path, in one 16- or 32-token dense pass, else in 64-token wide passes.
 template <int MODE, int Q>
 MOE_INLINE void run_item(const KArgs& A, const Item& it, const Queue& Qu) {
-  if (it.n > 2 * kDenseGroup) run_item_wide<MODE, Q, kWideTok>(A, it, Qu);
+  if (it.n > 2 * kDenseGroup) run_item_wide<MODE, Q>(A, it, Qu);
   else if (it.n > kDenseGroup) run_item_dense<MODE, Q, 32>(A, it, Qu);
   else run_item_dense<MODE, Q, 16>(A, it, Qu);
 }
