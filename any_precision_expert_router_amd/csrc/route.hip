@@ -18,50 +18,12 @@
 // grouping also accepts ids it did not produce: an id outside [0, E) is not placed, and a token
 // that names an expert twice is placed in slot order.
 #include "internal.hpp"
+#include "wave_ops.hpp"
 
 namespace moeapq {
 namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread workgroup
-
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;  // -0.0 ties with +0.0
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(e));
-}
-
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t ord = static_cast<uint32_t>(key >> 32);
-  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
-  return __uint_as_float(u);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t max_dpp(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v), CTRL, 0xf, 0xf, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(v >> 32), CTRL, 0xf, 0xf, false);
-  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-  return o > v ? o : v;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), lane);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), lane);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
-// Wavefront maximum of a 64-bit key, returned uniform: DPP butterflies inside each 16-lane row
-// (quad swaps, then half-row and row mirrors), then the four row maxima through scalar registers.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v = max_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v = max_dpp<0x141>(v);  // row_half_mirror
-  v = max_dpp<0x140>(v);  // row_mirror
-  const uint64_t a = readlane64(v, 0), b = readlane64(v, 16), c = readlane64(v, 32), d = readlane64(v, 48);
-  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
-  return ab > cd ? ab : cd;
-}
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
@@ -79,7 +41,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + 64 * i;
-    key[i] = e < E ? route_key(row[e], e) : 0ull;  // real keys are never 0
+    key[i] = e < E ? order_key(row[e], e) : 0ull;  // real keys are never 0
   }
   uint64_t mine = 0ull;  // lane j keeps the key chosen in round j
   for (int j = 0; j < k; ++j) {
@@ -92,11 +54,11 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
       if (key[i] == win) key[i] = 0ull;  // unique: ids differ
     if (lane == j) mine = win;
   }
-  const float l0 = key_logit(readlane64(mine, 0));
-  const float z = lane < k ? expf(key_logit(mine) - l0) : 0.0f;
+  const float l0 = key_value(readlane64(mine, 0));
+  const float z = lane < k ? expf(key_value(mine) - l0) : 0.0f;
   const float s = wave_sum_f32(z);
   if (lane < k) {
-    const int32_t id = static_cast<int32_t>(~static_cast<uint32_t>(mine));
+    const int32_t id = key_id(mine);
     ids_out[lane] = id;
     gates_out[lane] = z / s;
     if (ids_copy) ids_copy[lane] = id;

@@ -474,7 +474,9 @@ def next_rows(apq, torch, call, base, dev, n):
     out["substitution"] = {
         "us_per_call": round(us, 3), "policy": "0.15 rule + background admission at 0.5",
         "substituted_slots": int((missed >= 0).sum()), "fetched_experts": int(fetch.sum()),
-        "note": "one workgroup, a wavefront per token; a quarter of the experts resident"}
+        "note": "a wavefront per token (one workgroup up to 16 tokens; beyond, four tokens per "
+                "workgroup, then one workgroup for the fetch flags and admission); a quarter of "
+                "the experts resident"}
     log(f"[bench] substitution: {us:.2f} us per call")
 
     ids_l = ids_in.unsqueeze(0).repeat(n + 1, 1, 1)
