@@ -297,6 +297,27 @@ def test_layer_long_down_rows_split_into_segments(threshold):
     _check_layer(shape, q_override=q, threshold=threshold)
 
 
+def test_layer_output_at_an_unaligned_address():
+    """y given 2 bytes past an 8-byte boundary: the combine stores it element by element, with the
+    same values as into an aligned buffer."""
+    shape = wl.TINY.replace(H=256, E=8, I=256, k=2, T=9, I_shared=512, q_shared=8, name="unaligned y")
+    inputs = wl.gen_layer_inputs(shape)
+    dl = gpu_layers.device_layer(shape)
+    y_aligned, _ = _run_layer(shape, inputs, dl)
+    T = shape.T
+    buf = torch.zeros(T * shape.H + 4, dtype=torch.float16, device=DEV)
+    y = buf[1:1 + T * shape.H].view(T, shape.H)
+    assert y.data_ptr() % 8 == 2
+    ws = torch.zeros(apq.moe_workspace_bytes(T, shape.E, shape.H, shape.I, shape.k, shape.I_shared),
+                     dtype=torch.uint8, device=DEV)
+    apq.moe_layer_forward(_t(inputs.logits), _t(inputs.x), shape.E, shape.H, shape.I, shape.k, dl.table,
+                          y, ws, shared=dl.shared, I_shared=shape.I_shared)
+    apq.moe_check_device_error(ws)
+    got = buf.cpu().numpy()
+    assert got[0] == 0 and got[-3:].tolist() == [0, 0, 0]   # nothing written outside y
+    np.testing.assert_array_equal(y.float().cpu().numpy().astype(np.float64), y_aligned)
+
+
 def test_layer_k1_and_k_equals_E():
     _check_layer(wl.TINY.replace(k=1, T=9, name="k=1"))
     _check_layer(wl.TINY.replace(k=8, T=6, name="k=E"))
