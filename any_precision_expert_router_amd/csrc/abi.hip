@@ -111,7 +111,7 @@ Workspace carve_workspace(void* base, int T, int E, int H, int I, int k, int I_s
   const size_t o_part = take(w.segs * TK * H * sizeof(float));
   const size_t o_part_sh =
       take(I_shared > 0 ? w.segs_shared * static_cast<size_t>(T) * H * sizeof(float) : 0);
-  const size_t o_recs = take(max_records(T, E, k) * sizeof(ExpertRecord));
+  const size_t o_recs = take(2 * max_records(T, E, k) * sizeof(ExpertRecord));
   const size_t o_ctr = take(kNumCounters * sizeof(uint32_t));
   const size_t o_nrecs = take(sizeof(int32_t));
   w.bytes = off;

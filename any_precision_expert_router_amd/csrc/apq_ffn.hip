@@ -34,6 +34,7 @@ int launch_apq_ffn(const FfnArgs& a, hipStream_t stream) {
   k.counter = a.ws.counters + kCtrGateUp;
   if (int rc = apq::launch_gate_up(k, gu_items, stream)) return rc;
   k.counter = a.ws.counters + kCtrDown;
+  k.recs = a.ws.recs + max_records(a.T, a.E, a.k);   // the down kernel's record order
   k.segs = a.ws.segs;
   k.segs_shared = sh ? a.ws.segs_shared : 1;
   const int dn_items = (sh * k.segs_shared + routed * k.segs) * (a.H / kRowPanel);

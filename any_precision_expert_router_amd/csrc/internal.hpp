@@ -54,8 +54,9 @@ constexpr int kRecTok = 4;   // tokens described in full (the streaming path's g
 // workgroup looping over its token groups.  Records of multi-token experts come first (their
 // items are the longest), then the streaming ones, each class in active-list order.
 constexpr int kRecGroupTok = 64;
+constexpr int kRecDensePassTok = 32;   // the most tokens one dense matrix-core pass holds
 constexpr int kRecSplitMaxPairs = 1024;
-inline size_t max_records(int T, int E, int k) {
+__host__ __device__ inline size_t max_records(int T, int E, int k) {
   return static_cast<size_t>(E) + 2 + (static_cast<size_t>(T) * k + kRecGroupTok - 1) / kRecGroupTok;
 }
 struct alignas(128) ExpertRecord {
@@ -104,7 +105,7 @@ struct Workspace {
   float* part;           // fp32 [segs][T*k][H]  gate-scaled expert outputs, pair order
   float* part_shared;    // fp32 [segs_sh][T][H] scaled shared-expert outputs
   int segs, segs_shared; // down column segments (down_segments)
-  ExpertRecord* recs;    // [max_records(T, E, k)]
+  ExpertRecord* recs;    // [2][max_records(T, E, k)]: one record order per module (gate_up, down)
   int32_t* n_recs;       // [1] routed records of the call
   uint32_t* counters;    // [kNumCounters]
   size_t bytes;          // total bytes the layout needs
@@ -140,7 +141,7 @@ struct RecordArgs {
   const moe_apq_block* shared;
   const float* gates;          // [T*k] gate weights (written by routing in the same launch or before)
   int E, H, I, I_shared, T, k;
-  ExpertRecord* recs;
+  ExpertRecord* recs;          // [2][max_records(T, E, k)]
   uint32_t* counters;
   int32_t* n_recs;             // out: routed records written (records 1 .. n_recs)
   int dense_threshold;         // the FFN's effective threshold (orders the records)

@@ -89,6 +89,7 @@ struct GroupSmem {
   int32_t dup_tag[kGroupMapBytes / 4];    // large batches: [segments][E] last token that named e
   int32_t offsets[MOE_MAX_EXPERTS + 1];  // LDS copies of the grouping results for the records
   int32_t active[MOE_MAX_EXPERTS];
+  int32_t qslot[2][4][18];                // records: per module, class and order bucket, counts then positions
   int32_t n_active;
 };
 
@@ -313,10 +314,11 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
     streaming = n <= kRecTok && n < r.dense_threshold;
     groups = !streaming && split && n > kRecGroupTok ? (n + kRecGroupTok - 1) / kRecGroupTok : 1;
   }
-  // exclusive scans of the records of multi-token experts, then of the streaming experts in three
-  // classes by token count (3-4, 2, 1): a streaming workgroup keeps its ring across consecutive
-  // items whose token count fits the ring's, so equal counts are kept together
+  // record totals of the four classes: the multi-token experts, then the streaming experts by
+  // token count (3-4, 2, 1) -- a streaming workgroup keeps its ring across consecutive items
+  // whose token count fits the ring's, so equal counts are kept together
   const bool act_ = tid < n_act;
+  for (int i = tid; i < 2 * 4 * 18; i += blockDim.x) (&sm.qslot[0][0][0])[i] = 0;
   int v[4] = {act_ && !streaming ? groups : 0, act_ && streaming && n >= 3 ? 1 : 0,
               act_ && streaming && n == 2 ? 1 : 0, act_ && streaming && n == 1 ? 1 : 0};
   const int v0[4] = {v[0], v[1], v[2], v[3]};
@@ -334,12 +336,11 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
     for (int c = 0; c < 4; ++c) sm.wave_tot[c][wave] = v[c];
   }
   __syncthreads();
-  int cbase[4] = {0, 0, 0, 0}, tot[4] = {0, 0, 0, 0};
+  int tot[4] = {0, 0, 0, 0};
   for (int w = 0; w < static_cast<int>(blockDim.x) / 64; ++w) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int t = sm.wave_tot[c][w];
-      if (w < wave) cbase[c] += t;
       tot[c] += t;
     }
   }
@@ -351,10 +352,40 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     if (c < cls) first += tot[c];
+  // Per module, each class's records are ordered roughly by cost, costliest first, so that the
+  // queue hands out the longest items first and the tail once it runs dry is shorter: the
+  // matrix-core records with wide passes (more than 32 tokens) first, then by that module's
+  // width, widest first.  Consecutive streaming items then also share a width more often (their
+  // ring continues only across items of one width).  Positions inside a bucket come from LDS
+  // atomics: the order only schedules work, every item's result is the same.
+  ExpertRecord rec;
+  int bk[2] = {0, 0};
   if (tid < n_act) {
-    const int pos = first + cbase[cls] + v[cls] - v0[cls];
-    ExpertRecord rec;
     fill_record(rec, r.table[2 * e], r.table[2 * e + 1], r.I, r);
+    const bool ok = record_ok(rec.meta);
+    const bool wide = cls == 0 && n > kRecDensePassTok;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bk[m] = (ok ? record_q(rec.meta, m) : 0) + (wide ? 9 : 0);
+      atomicAdd(&sm.qslot[m][cls][bk[m]], groups);
+    }
+  }
+  __syncthreads();
+  if (tid < 8) {
+    const int m = tid >> 2, c = tid & 3;
+    int run = 0;
+    for (int b = 17; b >= 0; --b) {
+      const int cnt = sm.qslot[m][c][b];
+      sm.qslot[m][c][b] = run;
+      run += cnt;
+    }
+  }
+  __syncthreads();
+  if (tid < n_act) {
+    int pos_m[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) pos_m[m] = first + atomicAdd(&sm.qslot[m][cls][bk[m]], groups);
+    const size_t stride = max_records(r.T, r.E, r.k);
     rec.expert = e;
     for (int g = 0; g < groups; ++g) {
       rec.src_base = base + g * kRecGroupTok;
@@ -366,12 +397,13 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
         rec.tok[t] = p / r.k;
         rec.gate[t] = t < rec.n ? gates[p] : 0.0f;
       }
-      r.recs[1 + pos + g] = rec;
+      r.recs[1 + pos_m[0] + g] = rec;
+      r.recs[stride + 1 + pos_m[1] + g] = rec;
     }
   }
   if (tid == 0) {
     r.n_recs[0] = tot[0] + tot[1] + tot[2] + tot[3];
-    ExpertRecord rec{};
+    rec = ExpertRecord{};
     if (r.shared) {
       fill_record(rec, r.shared[0], r.shared[1], r.I_shared, r);
     } else {
@@ -387,6 +419,7 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
       rec.gate[t] = 1.0f;
     }
     r.recs[0] = rec;
+    r.recs[max_records(r.T, r.E, r.k)] = rec;
   }
   for (int c = tid; c < kNumCounters; c += blockDim.x) r.counters[c] = 0u;
   if (r.err_clear && tid < 3) r.err_clear[tid] = 0;   // the FFN launches of this call set it
