@@ -188,8 +188,10 @@ struct KArgs {
   uint32_t* counter;            // work counter of this launch (null: static round-robin)
 };
 
-// Work queue of a workgroup.  Its first two items are blockIdx.x and blockIdx.x + gridDim.x;
-// the later ones come from its sub-queue's counter, requested by thread 0 one item ahead and
+// Work queue of a workgroup.  Its first item is blockIdx.x; its second is 2 gridDim.x - 1 -
+// blockIdx.x when the launch has at least two items per workgroup (the records are ordered
+// costliest first, so a workgroup whose first item is among the longest gets a second one among
+// the shorter), else blockIdx.x + gridDim.x; the later ones come from its sub-queue's counter, requested by thread 0 one item ahead and
 // published to the workgroup through LDS at the current item's reduction barrier, so the
 // atomic's latency hides behind a whole item.  Without a counter the queue is static
 // round-robin.  Everything the publish step needs is computed once here, so that step reads no
@@ -204,11 +206,12 @@ struct Queue {
 
 // The dynamic items (from 2 * gridDim.x on) are dealt to min(kQueues, gridDim.x) interleaved
 // sub-queues, each with its own counter, so that no single address takes every fetch.
-MOE_INLINE void queue_init(const KArgs& A, Queue& Qu) {
+MOE_INLINE void queue_init(const KArgs& A, Queue& Qu, int total) {
   const int grid = static_cast<int>(gridDim.x);
   const int nsub = min(kQueues, grid);
   const int sub = static_cast<int>(blockIdx.x) % nsub;
-  Qu.nxt = static_cast<int>(blockIdx.x) + grid;
+  const int b = static_cast<int>(blockIdx.x);
+  Qu.nxt = total >= 2 * grid ? 2 * grid - 1 - b : b + grid;
   Qu.dynamic = A.counter != nullptr;
   Qu.base = Qu.dynamic ? 2 * grid + sub : 0;
   Qu.stride = Qu.dynamic ? nsub : grid;
@@ -1513,7 +1516,7 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
   const int srt = MODE == kDown ? A.segs : 1;
   const int total = sh_tiles * ssh + n_routed * tiles * srt;
   Queue Qu;
-  queue_init(A, Qu);
+  queue_init(A, Qu, total);
   queue_request(Qu);
   int i = static_cast<int>(blockIdx.x);
   Item it;
