@@ -90,6 +90,7 @@ struct GroupSmem {
   int32_t offsets[MOE_MAX_EXPERTS + 1];  // LDS copies of the grouping results for the records
   int32_t active[MOE_MAX_EXPERTS];
   int32_t qslot[2][4][18];                // records: per module, class and order bucket, counts then positions
+  int32_t cls_tot[4];                     // records: per class
   int32_t n_active;
 };
 
@@ -97,7 +98,7 @@ struct GroupSmem {
 // workgroup before a barrier.  SEGMENTED picks the placement: a segmented counting sort (large
 // batches: every wavefront places its own run of tokens), or a token x expert slot map walked by
 // one thread per expert (small batches, where it measured faster).
-template <bool SEGMENTED>
+template <bool SEGMENTED, bool DISTINCT = false>
 __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ pairs, int32_t* __restrict__ active,
                            int32_t* __restrict__ n_active, GroupSmem& sm, int32_t* pairs_lds) {
@@ -161,7 +162,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
     const int seg_len = (T + S - 1) / S;
     for (int i = tid; i < S * E; i += kGroupThreads) {
       sm.seg_pos[i] = 0;
-      sm.dup_tag[i] = -1;
+      if constexpr (!DISTINCT) sm.dup_tag[i] = -1;
     }
     __syncthreads();
     const int t_begin = min(T, wave * seg_len), t_end = min(T, t_begin + seg_len);
@@ -192,11 +193,12 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
         // Two slots of one token naming the same expert: each valid slot swaps its token into
         // the expert's tag; the later of two such slots gets its own token back.  The swaps of
         // a token complete before the next token's (one LDS instruction each, in order).
+        // (ids the caller guarantees distinct per token, DISTINCT, skip the swaps)
         bool clash[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const bool valid = static_cast<unsigned>(e[u]) < static_cast<unsigned>(E);
-          clash[u] = valid && atomicExch(&tag_of[valid ? e[u] : 0], t0 + u) == t0 + u;
+          clash[u] = !DISTINCT && valid && atomicExch(&tag_of[valid ? e[u] : 0], t0 + u) == t0 + u;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -204,7 +206,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
             const int p = (t0 + u) * k + lane;
             const int eu = e[u];
             const bool valid = static_cast<unsigned>(eu) < static_cast<unsigned>(E);
-            if (__ballot(clash[u]) == 0) {
+            if (DISTINCT || __ballot(clash[u]) == 0) {
               // distinct experts: the token's slots never share a position counter
               if (valid) {
                 const int pos = pos_of[eu];
@@ -319,31 +321,19 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
   // whose token count fits the ring's, so equal counts are kept together
   const bool act_ = tid < n_act;
   for (int i = tid; i < 2 * 4 * 18; i += blockDim.x) (&sm.qslot[0][0][0])[i] = 0;
-  int v[4] = {act_ && !streaming ? groups : 0, act_ && streaming && n >= 3 ? 1 : 0,
-              act_ && streaming && n == 2 ? 1 : 0, act_ && streaming && n == 1 ? 1 : 0};
-  const int v0[4] = {v[0], v[1], v[2], v[3]};
+  if (tid < 4) sm.cls_tot[tid] = 0;
+  const int v0[4] = {act_ && !streaming ? groups : 0, act_ && streaming && n >= 3 ? 1 : 0,
+                     act_ && streaming && n == 2 ? 1 : 0, act_ && streaming && n == 1 ? 1 : 0};
+  __syncthreads();  // the grouping's last reads of its LDS are done; the counters are zero
+  if (act_) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int o = __shfl_up(v[c], off, 64);
-      if (lane >= off) v[c] += o;
-    }
-  }
-  __syncthreads();  // the grouping's last reads of wave_tot are done
-  if (lane == 63) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) sm.wave_tot[c][wave] = v[c];
+    for (int c = 0; c < 4; ++c)
+      if (v0[c]) atomicAdd(&sm.cls_tot[c], v0[c]);
   }
   __syncthreads();
-  int tot[4] = {0, 0, 0, 0};
-  for (int w = 0; w < static_cast<int>(blockDim.x) / 64; ++w) {
+  int tot[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int t = sm.wave_tot[c][w];
-      tot[c] += t;
-    }
-  }
+  for (int c = 0; c < 4; ++c) tot[c] = sm.cls_tot[c];
   int cls = 0;
 #pragma unroll
   for (int c = 1; c < 4; ++c)
@@ -452,7 +442,8 @@ __global__ __launch_bounds__(kGroupThreads) void group_records_kernel(
     const int32_t* __restrict__ ids, int32_t* __restrict__ offsets, int32_t* __restrict__ pairs,
     int32_t* __restrict__ active, int32_t* __restrict__ n_active, RecordArgs r) {
   __shared__ GroupSmem sm;
-  group_body<true>(ids, r.T, r.k, r.E, offsets, pairs, active, n_active, sm, nullptr);
+  // the ids come from route_topk: every token names k distinct experts
+  group_body<true, true>(ids, r.T, r.k, r.E, offsets, pairs, active, n_active, sm, nullptr);
   __syncthreads();
   records_body(sm, pairs, r.gates, r);
 }
