@@ -52,6 +52,25 @@ MOE_INLINE const AS_GLOBAL T* gview(const void* p) { return (const AS_GLOBAL T*)
 template <class T>
 MOE_INLINE const AS_CONST T* cview(const void* p) { return (const AS_CONST T*)p; }
 
+// Buffer resource over `bytes` bytes at `base` (both wavefront-uniform; below 4 GiB: the host
+// refuses larger activation arrays and weight blocks).  Loads past the end return zeros.
+//
+// The matrix-core branches load everything they stream (plane words, LUT rows, the token indices
+// of their rows, and the activations they stage straight into LDS) with buffer instructions, and
+// only those, while a tile's loads are in flight.  Their waits are partial counts ("all but the
+// next chunk's loads"), which hold only if the loads they count complete in issue order; the
+// staging loads have to be buffer loads (the global-address form is a FLAT-family instruction that
+// also accesses LDS, after which the compiler waits for every outstanding load at the next use of
+// a loaded register, draining the chunk ring every iteration), and mixing them with global-address
+// loads in flight gave stale staged activations.
+MOE_INLINE __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(static_cast<uint32_t>(bytes)), 0x00020000);
+}
+MOE_INLINE uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 constexpr int kThreads = 64 * kWavesPerTile;
 constexpr int kMaxTokGroup = 4;                  // tokens sharing one VALU pass over the weights
 constexpr int kDenseGroup = 16;                  // tokens of the smaller dense MFMA pass (32x32 tile)
@@ -245,8 +264,28 @@ MOE_INLINE int lane_row(const Item& it, int lane) {
 // Each thread prefetches LUT bytes of its lane's row into registers (only those it needs):
 //   q <= 4: the whole row (2^q fp16, at most 32 bytes), every wavefront;
 //   q >= 5: quarter `wave` of the row (2^(q-2) fp16, at most 128 bytes).
-template <int Q>
+template <int Q, bool BUF = false>
 MOE_INLINE void prefetch_lut_q(const Item& it, int lane, int wave, u32x4 (&L)[kLutRegs]) {
+  if constexpr (BUF) {   // the same bytes through buffer loads (matrix-core branches)
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(it.lut, static_cast<size_t>(it.rows) * (2u << Q));
+    const uint32_t o = static_cast<uint32_t>(lane_row(it, lane)) * (2u << Q);
+    if constexpr (Q == 1) {
+      L[0].x = buf_u32(r, o);
+    } else if constexpr (Q == 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0);
+      L[0].x = v.x;
+      L[0].y = v.y;
+    } else if constexpr (Q <= 4) {
+#pragma unroll
+      for (int q = 0; q < (1 << (Q - 3)); ++q) L[q] = __builtin_amdgcn_raw_buffer_load_b128(r, o + 16u * q, 0, 0);
+    } else {
+      constexpr int n4 = 1 << (Q - 5);
+      const uint32_t ow = o + static_cast<uint32_t>(wave) * (16u * n4);
+#pragma unroll
+      for (int q = 0; q < n4; ++q) L[q] = __builtin_amdgcn_raw_buffer_load_b128(r, ow + 16u * q, 0, 0);
+    }
+    return;
+  }
   const AS_GLOBAL char* g = gview<char>(reinterpret_cast<const char*>(it.lut) +
                                         static_cast<size_t>(lane_row(it, lane)) * (2u << Q));
   if constexpr (Q == 1) {
@@ -696,16 +735,31 @@ MOE_INLINE void decode_word_dense(const uint32_t (&w)[Q], uint32_t lane4, uint32
   dense_finish<Q>(v, wv);
 }
 
-// 16 bytes per lane from `src` straight into LDS at lds_addr + 16 * lane (a global load in its
-// LDS-DMA form).  The compiler sees it as a vector-memory load, so its own waits for later-used
-// registers count it; what it does not model is the LDS write, so readers of the staged bytes
-// wait by hand (dense_wait / wide_wait) and a slot is refilled only after an lgkmcnt(0).
-MOE_INLINE void lds_dma16(uint32_t lds_addr, const AS_GLOBAL char* src) {
-  __builtin_amdgcn_global_load_lds(src, (AS_LDS void*)(static_cast<uintptr_t>(lds_addr)), 16, 0, 0);
+// 16 bytes per lane from byte voff + soff of the buffer `rsrc` straight into LDS at lds_addr +
+// 16 * lane (a buffer load in its LDS-DMA form).  The compiler sees it as a vector-memory load, so
+// its own waits for later-used registers count it; what it does not model is the LDS write, so
+// readers of the staged bytes wait by hand (dense_wait / wide_wait) and a slot is refilled only
+// after an lgkmcnt(0).  The global-address form of this load belongs to the FLAT family and also
+// accesses LDS; after one of those the compiler waits for every outstanding vector-memory
+// operation at the next use of a loaded register, which drained the chunk ring at every loop
+// iteration.  The buffer form keeps the compiler's waits exact.
+MOE_INLINE void lds_dma16(uint32_t lds_addr, __amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (AS_LDS void*)(static_cast<uintptr_t>(lds_addr)), 16, voff,
+                                           soff, 0, 0);
 }
+
 
 // The LDS reads of a ring slot's previous chunk have returned (it is about to be refilled).
 MOE_INLINE void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
+// Keeps the loads issued before it ahead of those issued after it.  The partial waits count a
+// slot's loads as one group in slot order: if the compiler interleaved two slots' loads (it
+// scheduled both slots' plane loads ahead of both slots' staging loads once), "all but the next
+// slot's loads" would no longer cover the current slot's staging.
+MOE_INLINE void issue_order() {
+  asm volatile("" : : : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // A dense pass holds NT = 16 or 32 tokens.  Its chunk is 128 columns (a lane's 16-byte plane
 // unit, 4 words) for 16 tokens and 64 columns (half a unit, 2 words) for 32 tokens, so that a
@@ -731,30 +785,40 @@ struct DenseStream {
   static constexpr uint32_t kPieceBytes = NT * 16;       // one 8-column piece of every token
   typedef typename PlaneUnit<NT>::type unit_t;
   unit_t buf[D][Q];                 // plane words of a chunk
-  const AS_GLOBAL unit_t* pbase;    // the lane's unit of chunk 0 of plane 0
-  size_t plane_units;               // plane stride in units
+  __amdgpu_buffer_rsrc_t prsrc;     // the block's first Q bit planes
+  uint32_t poff;                    // per lane: byte of its unit in chunk 0 of plane 0
+  uint32_t plane_bytes;             // plane stride
   int cb, ce;                       // this wavefront's chunks [cb, ce)
-  const AS_GLOBAL char* xsrc;       // per lane: DMA 0's source in chunk 0
+  __amdgpu_buffer_rsrc_t xrsrc;     // the activation rows
+  uint32_t xoff;                    // per lane: DMA 0's source byte in chunk 0
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, piece 0
 
   // Loads are issued unconditionally (a chunk past the end re-reads the last one, a cache hit)
   // so that the number of loads in flight is always the same.
   MOE_INLINE int clamp(int c) const { return c < ce ? c : (ce > cb ? ce - 1 : cb); }
-  MOE_INLINE const AS_GLOBAL unit_t* unit_of(int c) const {
+  // Byte offset of chunk c from the lane's unit of chunk 0 (a 128-column chunk is one 1-KiB run of
+  // the 64 rows' units; a 64-column chunk is half c & 1 of every unit of run c >> 1).
+  MOE_INLINE uint32_t chunk_off(int c) const {
     if constexpr (NT == 16) {
-      return pbase + static_cast<size_t>(c) * 64;
-    } else {   // 64-column chunk c: half c & 1 of 16-byte unit c >> 1
-      return pbase + static_cast<size_t>(c >> 1) * 128 + (c & 1);
+      return static_cast<uint32_t>(c) * 1024u;
+    } else {
+      return static_cast<uint32_t>(c >> 1) * 1024u + static_cast<uint32_t>(c & 1) * 8u;
     }
   }
   // The refill of slot `slot` with chunk c: its Q plane loads (registers), then its kDma staged
   // activation loads (LDS), on every path.  The plane loads may go out as soon as the slot's
   // plane words are consumed; the staging waits until the slot's B reads have returned.
   MOE_INLINE void issue_planes(int slot, int c) {
-    const AS_GLOBAL unit_t* u = unit_of(c);
+    const uint32_t co = chunk_off(c);
 #pragma unroll
-    for (int p = 0; p < Q; ++p) buf[slot][p] = u[p * plane_units];
+    for (int p = 0; p < Q; ++p) {
+      if constexpr (NT == 16) {
+        buf[slot][p] = __builtin_amdgcn_raw_buffer_load_b128(prsrc, poff, co + p * plane_bytes, 0);
+      } else {
+        buf[slot][p] = __builtin_amdgcn_raw_buffer_load_b64(prsrc, poff, co + p * plane_bytes, 0);
+      }
+    }
   }
   MOE_INLINE void issue_stage(int slot, int c) {
     lds_reads_done();
@@ -762,11 +826,14 @@ struct DenseStream {
     constexpr int kChunkBytes = kWords * 32 * 2;               // bytes of a token row per chunk
 #pragma unroll
     for (int i = 0; i < kDma; ++i)
-      lds_dma16(xring + slot * kXSlotBytes + i * 1024, xsrc + i * kDmaStep + static_cast<size_t>(c) * kChunkBytes);
+      lds_dma16(xring + slot * kXSlotBytes + i * 1024, xrsrc, xoff, i * kDmaStep + static_cast<uint32_t>(c) * kChunkBytes);
   }
   MOE_INLINE void issue(int slot, int c) {
+    issue_order();
     issue_planes(slot, c);
+    issue_order();
     issue_stage(slot, c);
+    issue_order();
   }
   MOE_INLINE void prologue() {
 #pragma unroll
@@ -829,7 +896,7 @@ MOE_INLINE void dense_word_mma(const DenseWordOps<Q>& o, f32x16& lo, f32x16& hi)
 // last word's lookups and B reads are issued, the slot's registers and staged bytes are no
 // longer needed: its refill with chunk `next` goes out there, before the last two words'
 // products, which gives the refill that much more time to land.
-template <int Q, int NT>
+template <int Q, int NT, bool REFILL = true>
 MOE_INLINE void dense_chunk(DenseStream<Q, NT>& S, int s, int next, uint32_t lane4, f32x16& lo, f32x16& hi) {
   DenseWordOps<Q> a, b;
   dense_word_lookup<Q, NT, 0>(S, s, lane4, a);
@@ -844,17 +911,21 @@ MOE_INLINE void dense_chunk(DenseStream<Q, NT>& S, int s, int next, uint32_t lan
     __builtin_amdgcn_sched_barrier(0);
     dense_word_lookup<Q, NT, 3>(S, s, lane4, b);
     __builtin_amdgcn_sched_barrier(0);
-    if (next >= 0) S.issue_planes(s, next);
+    if (REFILL) S.issue_planes(s, next);
     __builtin_amdgcn_sched_barrier(0);
     dense_word_mma<Q>(a, lo, hi);
     __builtin_amdgcn_sched_barrier(0);
     dense_word_mma<Q>(b, lo, hi);
   } else {
-    if (next >= 0) S.issue_planes(s, next);
+    if (REFILL) S.issue_planes(s, next);
     __builtin_amdgcn_sched_barrier(0);
     dense_word_mma<Q>(b, lo, hi);
   }
-  if (next >= 0) S.issue_stage(s, next);
+  if (REFILL) {
+    issue_order();
+    S.issue_stage(s, next);
+    issue_order();
+  }
 }
 
 template <int Q, int NT>
@@ -872,43 +943,49 @@ MOE_INLINE void dense_columns(DenseStream<Q, NT>& S, uint32_t lane4, f32x16& lo,
   }
   if (c < S.ce) {
     dense_wait<Q, NT>();
-    dense_chunk<Q, NT>(S, 0, -1, lane4, lo, hi);
+    dense_chunk<Q, NT, false>(S, 0, -1, lane4, lo, hi);
   }
 }
 
 // Geometry of the tile for this wavefront and the activation rows of tokens [g0, g0 + ng).
 template <int MODE, int Q, int NT>
 MOE_INLINE void make_dense_stream(const KArgs& A, const Item& it, int g0, int ng, DenseStream<Q, NT>& S) {
-  typedef typename DenseStream<Q, NT>::unit_t unit_t;
   constexpr int kPer = 4 / DenseStream<Q, NT>::kWords;   // chunks per 128 columns
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int C = it.cols;
   const int row = lane_row(it, lane);
   const int nc4 = C / kColChunk;
-  S.pbase = gview<unit_t>(it.planes) + (static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel)) * kPer;
-  S.plane_units = static_cast<size_t>(it.rows) * C / (32 * DenseStream<Q, NT>::kWords);
+  S.plane_bytes = static_cast<uint32_t>(static_cast<size_t>(it.rows) * C / 8);
+  S.prsrc = buf_rsrc(it.planes, static_cast<size_t>(S.plane_bytes) * Q);
+  S.poff = static_cast<uint32_t>((row / kRowPanel) * nc4 * 64 + (row % kRowPanel)) * 16u;
   S.cb = uniform(kPer * it.c0 + (kPer * it.nc * wave) / kWavesPerTile);
   S.ce = uniform(kPer * it.c0 + (kPer * it.nc * (wave + 1)) / kWavesPerTile);
   const uint16_t* base;   // the activation rows: x (gate_up, plain) or act (down)
+  int rows_total;
   if constexpr (MODE == kDown) {
     base = it.shared ? A.act_shared : A.act;
+    rows_total = it.shared ? A.T : A.T * A.k;
   } else {
     base = A.x;
+    rows_total = A.T;
   }
   // token lane % NT (tokens past ng re-read token g0's row: their columns are never stored)
   const int t = lane & (NT - 1);
   const int tt = g0 + (t < ng ? t : 0);
   int row_index;
   if constexpr (MODE == kGateUp) {
-    row_index = it.shared ? tt : A.pairs[it.src_base + tt] / A.k;
+    row_index = it.shared ? tt
+                          : static_cast<int>(buf_u32(buf_rsrc(A.pairs, static_cast<size_t>(A.T) * A.k * 4),
+                                                     static_cast<uint32_t>(it.src_base + tt) * 4u)) / A.k;
   } else if constexpr (MODE == kDown) {
     row_index = it.shared ? tt : it.src_base + tt;
   } else {
     row_index = tt;
   }
   // DMA lane l: token l % NT, piece l / NT of the DMA's group of 64 / NT pieces
-  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + (lane / NT) * 16;
+  S.xrsrc = buf_rsrc(base, static_cast<size_t>(rows_total) * C * 2);
+  S.xoff = static_cast<uint32_t>(row_index) * static_cast<uint32_t>(C * 2) + (lane / NT) * 16;
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
   S.bx = S.xring + static_cast<uint32_t>(lane & (NT - 1)) * 16u + static_cast<uint32_t>(lane >> 5) * DenseStream<Q, NT>::kPieceBytes;
 }
@@ -1025,10 +1102,10 @@ template <int MODE, int Q, int NT>
 MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  u32x4 L[kLutRegs];
-  prefetch_lut_q<Q>(it, lane, wave, L);
   DenseStream<Q, NT> S;
   make_dense_stream<MODE, Q, NT>(A, it, 0, min(NT, it.n), S);
+  u32x4 L[kLutRegs];
+  prefetch_lut_q<Q, true>(it, lane, wave, L);
   S.prologue();
   write_dense_table<Q>(L, lane, wave);
   __syncthreads();
@@ -1072,10 +1149,12 @@ struct WideStream {
   static constexpr int D = 2;       // chunks in flight per wavefront
   static constexpr int kDma = 4;    // staged loads per chunk: one per octet (lane = token)
   uint32_t buf[D][Q];               // this wavefront's plane word of the chunk, per plane
-  const AS_GLOBAL uint32_t* pbase;  // the lane's word in chunk 0 of plane 0
-  size_t plane_u32;                 // plane stride in 32-bit words
+  __amdgpu_buffer_rsrc_t prsrc;     // the block's first Q bit planes
+  uint32_t poff;                    // per lane: byte of its word in chunk 0 of plane 0
+  uint32_t plane_bytes;             // plane stride
   int cb, ce;                       // the item's chunks [cb, ce)
-  const AS_GLOBAL char* xsrc;       // per lane: its token's first staged octet of chunk 0
+  __amdgpu_buffer_rsrc_t xrsrc;     // the activation rows
+  uint32_t xoff;                    // per lane: its token's first staged octet of chunk 0
   uint32_t xring;                   // LDS address of this wavefront's ring
   uint32_t bx;                      // per lane: B-operand address in slot 0, octet 0, tile 0
 
@@ -1083,17 +1162,20 @@ struct WideStream {
   // The refill of slot `slot` with chunk c (see DenseStream).
   MOE_INLINE void issue_planes(int slot, int c) {
 #pragma unroll
-    for (int p = 0; p < Q; ++p) buf[slot][p] = pbase[p * plane_u32 + static_cast<size_t>(c) * 256];
+    for (int p = 0; p < Q; ++p) buf[slot][p] = buf_u32(prsrc, poff, static_cast<uint32_t>(c) * 1024u + p * plane_bytes);
   }
   MOE_INLINE void issue_stage(int slot, int c) {
     lds_reads_done();
 #pragma unroll
     for (int i = 0; i < kDma; ++i)
-      lds_dma16(xring + slot * kWideSlotBytes + i * 1024, xsrc + i * 16 + static_cast<size_t>(c) * 256);
+      lds_dma16(xring + slot * kWideSlotBytes + i * 1024, xrsrc, xoff, i * 16 + static_cast<uint32_t>(c) * 256);
   }
   MOE_INLINE void issue(int slot, int c) {
+    issue_order();
     issue_planes(slot, c);
+    issue_order();
     issue_stage(slot, c);
+    issue_order();
   }
   MOE_INLINE void prologue() {
 #pragma unroll
@@ -1117,28 +1199,35 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
   const int row = lane_row(it, lane);
   const int nc4 = C / kColChunk;
   // unit (panel, chunk 0, row) of plane 0, then this wavefront's 32-bit word inside it
-  S.pbase = gview<uint32_t>(it.planes) + (static_cast<size_t>(row / kRowPanel) * nc4 * 64 + (row % kRowPanel)) * 4 + wave;
-  S.plane_u32 = static_cast<size_t>(it.rows) * C / 32;
+  S.plane_bytes = static_cast<uint32_t>(static_cast<size_t>(it.rows) * C / 8);
+  S.prsrc = buf_rsrc(it.planes, static_cast<size_t>(S.plane_bytes) * Q);
+  S.poff = static_cast<uint32_t>((row / kRowPanel) * nc4 * 64 + (row % kRowPanel)) * 16u + wave * 4u;
   S.cb = it.c0;
   S.ce = it.c0 + it.nc;
   const uint16_t* base;   // the activation rows: x (gate_up, plain) or act (down)
+  int rows_total;
   if constexpr (MODE == kDown) {
     base = it.shared ? A.act_shared : A.act;
+    rows_total = it.shared ? A.T : A.T * A.k;
   } else {
     base = A.x;
+    rows_total = A.T;
   }
   // the lane's token (tokens past ng re-read token g0's row: their columns are never stored)
   const int t = lane;
   const int tt = g0 + (t < ng ? t : 0);
   int row_index;
   if constexpr (MODE == kGateUp) {
-    row_index = it.shared ? tt : A.pairs[it.src_base + tt] / A.k;
+    row_index = it.shared ? tt
+                          : static_cast<int>(buf_u32(buf_rsrc(A.pairs, static_cast<size_t>(A.T) * A.k * 4),
+                                                     static_cast<uint32_t>(it.src_base + tt) * 4u)) / A.k;
   } else if constexpr (MODE == kDown) {
     row_index = it.shared ? tt : it.src_base + tt;
   } else {
     row_index = tt;
   }
-  S.xsrc = gview<char>(base) + static_cast<size_t>(row_index) * C * 2 + wave * 64;
+  S.xrsrc = buf_rsrc(base, static_cast<size_t>(rows_total) * C * 2);
+  S.xoff = static_cast<uint32_t>(row_index) * static_cast<uint32_t>(C * 2) + wave * 64;
   S.xring = kXRingBase + static_cast<uint32_t>(wave) * kXWaveBytes;
   S.bx = S.xring + static_cast<uint32_t>(lane >> 5) * (kWideTok * 16) + static_cast<uint32_t>(lane & 31) * 16u;
 }
@@ -1146,7 +1235,7 @@ MOE_INLINE void make_wide_stream(const KArgs& A, const Item& it, int g0, int ng,
 // One chunk of ring slot s: this wavefront's 32-column word of it for the pass's tokens.  The B
 // reads are issued ahead of the table lookups (LDS operations complete in order), and the
 // lookups together (see dense_lookup).
-template <int Q>
+template <int Q, bool REFILL = true>
 MOE_INLINE void wide_chunk(WideStream<Q>& S, int s, int next, uint32_t lane4, int ntiles,
                            f32x16 (&lo)[kWideTiles], f32x16 (&hi)[kWideTiles]) {
   const char* xb = reinterpret_cast<const char*>(g_lds) + S.bx + s * kWideSlotBytes;
@@ -1162,7 +1251,7 @@ MOE_INLINE void wide_chunk(WideStream<Q>& S, int s, int next, uint32_t lane4, in
   uint32_t v[32];
   dense_lookup<Q>(w, lane4, v);
   __builtin_amdgcn_sched_barrier(0);
-  if (next >= 0) S.issue_planes(s, next);   // the slot's plane words are consumed
+  if (REFILL) S.issue_planes(s, next);   // the slot's plane words are consumed
   __builtin_amdgcn_sched_barrier(0);
   uint32_t wv[16];
   dense_finish<Q>(v, wv);
@@ -1186,7 +1275,11 @@ MOE_INLINE void wide_chunk(WideStream<Q>& S, int s, int next, uint32_t lane4, in
                                                     __builtin_bit_cast(half8_t, b[st][g]), hi[g], 0, 0, 0);
     }
   }
-  if (next >= 0) S.issue_stage(s, next);
+  if (REFILL) {
+    issue_order();
+    S.issue_stage(s, next);
+    issue_order();
+  }
 }
 
 template <int Q>
@@ -1203,7 +1296,7 @@ MOE_INLINE void wide_columns(WideStream<Q>& S, uint32_t lane4, int ntiles, f32x1
   }
   if (c < S.ce) {
     wide_wait<Q>();
-    wide_chunk<Q>(S, 0, -1, lane4, ntiles, lo, hi);
+    wide_chunk<Q, false>(S, 0, -1, lane4, ntiles, lo, hi);
   }
 }
 
@@ -1221,10 +1314,10 @@ template <int MODE, int Q>
 MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  u32x4 L[kLutRegs];
-  prefetch_lut_q<Q>(it, lane, wave, L);
   WideStream<Q> S;
   make_wide_stream<MODE, Q>(A, it, 0, min(kWideTok, it.n), S);
+  u32x4 L[kLutRegs];
+  prefetch_lut_q<Q, true>(it, lane, wave, L);
   S.prologue();
   write_dense_table<Q>(L, lane, wave);
   __syncthreads();
@@ -1480,7 +1573,12 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
     i = queue_advance(Qu);
     it = next;
     ok = next_ok;
-    if (!cont) return;
+    if (!cont) {
+      // the ring's filler loads (global-address form) land before a matrix-core item's buffer
+      // loads are issued: the partial waits there count only loads that complete in order
+      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      return;
+    }
     cur = nxt;
   }
 }
