@@ -152,6 +152,20 @@ MOE_INLINE uint32_t lds_load(uint32_t byte_addr) {
 
 MOE_INLINE int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Workgroup barrier for LDS traffic: every wavefront's LDS reads and writes (ds_*) complete
+// before it, while its vector-memory loads and stores stay in flight.  The tile kernels share data
+// between wavefronts only through LDS (tables, partial sums, the queue slot); a __syncthreads, and
+// a release fence on LDS alone once loads that write LDS directly are in flight, would wait for
+// every outstanding vector-memory operation too: the ring's prefetched chunks at the table
+// barrier, the tile's output stores at the reduction barriers.  Staged activations are never
+// read across wavefronts, and each wavefront waits for its own staging loads before it reads or
+// reuses its ring.  The memory clobbers keep the compiler from moving LDS accesses across.
+MOE_INLINE void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" : : : "memory");
+}
+
 MOE_INLINE uint32_t word_of(const u32x4& v, int jw) {
   return jw == 0 ? v.x : jw == 1 ? v.y : jw == 2 ? v.z : v.w;
 }
@@ -437,7 +451,7 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
     for (int t = 0; t < NT; ++t) red[((wave - 1) * kMaxTokGroup + t) * 64 + lane] = acc[t];
   }
   queue_publish(Qu);
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -472,7 +486,7 @@ MOE_INLINE void reduce_and_store(const KArgs& A, const Item& it, int g0, int ng,
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Item i of the launch's list: shared-expert tiles first (they carry every token), then the
@@ -1076,14 +1090,14 @@ MOE_INLINE void reduce_tile(const KArgs& A, const Item& it, int g0, int tok, boo
   }
   if (Qu) queue_publish(*Qu);
   const TileOut o = tile_out<MODE>(A, it, g0, tok, live);
-  __syncthreads();
+  lds_barrier();
   switch (wave) {
     case 0: reduce_quarter<MODE, 0>(lo, hi, ring, lane, o); break;
     case 1: reduce_quarter<MODE, 1>(lo, hi, ring, lane, o); break;
     case 2: reduce_quarter<MODE, 2>(lo, hi, ring, lane, o); break;
     default: reduce_quarter<MODE, 3>(lo, hi, ring, lane, o); break;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Columns l % 32 < 16 of a 16-token pass are token l % 16 (the other 16 repeat them); a 32-token
@@ -1108,7 +1122,7 @@ MOE_INLINE void run_item_dense(const KArgs& A, const Item& it, const Queue& Qu) 
   prefetch_lut_q<Q, true>(it, lane, wave, L);
   S.prologue();
   write_dense_table<Q>(L, lane, wave);
-  __syncthreads();
+  lds_barrier();
   for (int g0 = 0; g0 < it.n; g0 += NT) {
     const int ng = min(NT, it.n - g0);
     if (g0 > 0) {
@@ -1320,7 +1334,7 @@ MOE_INLINE void run_item_wide(const KArgs& A, const Item& it, const Queue& Qu) {
   prefetch_lut_q<Q, true>(it, lane, wave, L);
   S.prologue();
   write_dense_table<Q>(L, lane, wave);
-  __syncthreads();
+  lds_barrier();
   for (int g0 = 0; g0 < it.n; g0 += kWideTok) {
     const int ng = min(kWideTok, it.n - g0);
     if (g0 > 0) {
@@ -1549,7 +1563,7 @@ MOE_INLINE void valu_stream(const KArgs& A, Queue& Qu, int& i, Item& it, bool& o
     }
     cont = next_ok && next.q == Q && streamable<MODE>(A, next) && next.n <= NT;
     if (cont) make_geo<MODE>(A, next, nxt);
-    __syncthreads();
+    lds_barrier();
     if (cont) prefetch_lut_q<Q>(next, lane, wave, L);
     float acc[NT][4] = {};
     // the wavefront walks its chunks padded to a multiple of D, so the next item's chunk k
@@ -1624,7 +1638,7 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
       report_invalid(A, it, MODE);
       zero_skipped_rows<MODE>(A, it);
       queue_publish(Qu);
-      __syncthreads();
+      lds_barrier();
       i = queue_advance(Qu);
       ok = i < total && decode_item<MODE>(A, i, sh_tiles, tiles, it);
       continue;
