@@ -125,8 +125,9 @@ MOE_INLINE uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
 // Byte b of the result = q-bit index of column 8b + 2(o&3) + (o>>2) of this 32-column word.
 template <int Q>
 MOE_INLINE uint32_t single_word(const uint32_t (&w)[Q], int o) {
-  // the masks of planes 0..7 partition the word, so a chain of bit-field inserts merges them
-  uint32_t z = w[Q - 1] & plane_mask(Q - 1, o);
+  // the masks of planes 0..7 partition the word, so a chain of bit-field inserts merges them; with
+  // all eight planes every bit of the last plane outside its mask is overwritten by another plane
+  uint32_t z = Q == 8 ? w[Q - 1] : w[Q - 1] & plane_mask(Q - 1, o);
 #pragma unroll
   for (int p = Q - 2; p >= 0; --p) z = bfi(plane_mask(p, o), w[p], z);
   return rot(z, 8 - Q - o);
@@ -135,7 +136,8 @@ MOE_INLINE uint32_t single_word(const uint32_t (&w)[Q], int o) {
 // Byte b of the result = idx(8b + 2j) << 4 | idx(8b + 2j + 1)   (q <= 4).
 template <int Q>
 MOE_INLINE uint32_t pair_word(const uint32_t (&w)[Q], int j) {
-  uint32_t z = w[Q - 1] & (plane_mask(Q - 1, j) | plane_mask(Q - 1, j + 4));
+  // with four planes the eight masks (two per plane) partition the word, as in single_word at 8
+  uint32_t z = Q == 4 ? w[Q - 1] : w[Q - 1] & (plane_mask(Q - 1, j) | plane_mask(Q - 1, j + 4));
 #pragma unroll
   for (int p = Q - 2; p >= 0; --p) z = bfi(plane_mask(p, j) | plane_mask(p, j + 4), w[p], z);
   return rot(z, 4 - Q - j);
