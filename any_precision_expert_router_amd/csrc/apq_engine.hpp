@@ -22,10 +22,11 @@
 // is conflict-free whatever the indices, and the LDS address is one v_perm of the index byte
 // next to the lane offset.
 //
-// Products.  Tiles with at most 4 tokens stream: v_dot2c_f32_f16 (two MACs, fp32 accumulate)
-// against the token activations, broadcast across each 16-lane row by DPP.  Tiles with more
-// tokens use the matrix cores (v_mfma_f32_32x32x16_f16) on the decoded fp16 weights: the dense
-// branch takes 16 tokens per decode of the weights, the wide branch (prefill chunks) 64.
+// Products.  Tiles of 1 token, and of 2 tokens at widths <= 4 (takes_stream), stream:
+// v_dot2c_f32_f16 (two MACs, fp32 accumulate) against the token activations, broadcast across
+// each 16-lane row by DPP.  Other tiles use the matrix cores (v_mfma_f32_32x32x16_f16) on the
+// decoded fp16 weights: the dense branch takes 16 or 32 tokens per decode of the weights, the
+// wide branch (prefill chunks) 64.
 // Weights are never expanded to a dense matrix in memory.
 #pragma once
 #include "internal.hpp"
@@ -72,7 +73,7 @@ MOE_INLINE uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t so
 }
 
 constexpr int kThreads = 64 * kWavesPerTile;
-constexpr int kMaxTokGroup = 4;                  // tokens sharing one VALU pass over the weights
+constexpr int kMaxTokGroup = 2;                  // tokens sharing one VALU pass over the weights
 constexpr int kDenseGroup = 16;                  // tokens of the smaller dense MFMA pass (32x32 tile)
 
 // LDS map of a tile workgroup (bytes):
@@ -1365,7 +1366,7 @@ MOE_INLINE void run_item(const KArgs& A, const Item& it, const Queue& Qu) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Streaming across items (VALU tiles with at most 4 tokens).  Each wavefront keeps one ring of
+// Streaming across items (VALU tiles of 1 or 2 tokens).  Each wavefront keeps one ring of
 // in-flight chunks (planes + the tokens' activations) running across consecutive items of the
 // same width: while item i computes, the ring slots it frees are refilled with item i+1's
 // first chunks and item i+1's LUT rows are fetched into registers, so HBM stays busy through
@@ -1409,7 +1410,7 @@ MOE_INLINE void make_geo(const KArgs& A, const Item& it, Geo& G) {
   }
 }
 
-// NT: activation rows the ring loads per chunk (1, 2 or 4: the stream's largest token count).
+// NT: activation rows the ring loads per chunk (1 or 2: the stream's largest token count).
 template <int Q, int NT>
 struct Ring {
   static constexpr int D = ring_depth<Q>();
@@ -1497,8 +1498,9 @@ MOE_INLINE void ring_chunk(const Ring<Q, NT>& R, int s, int ng, uint32_t lane4,
 
 template <int MODE>
 MOE_INLINE bool streamable(const KArgs& A, const Item& it) {
-  return it.n <= kMaxTokGroup && it.n < A.dense_threshold;
+  return takes_stream(it.n, it.q, A.dense_threshold);
 }
+static_assert(kMaxTokGroup >= 2, "the streaming ring holds the largest streamed token count");
 
 MOE_INLINE void report_invalid(const KArgs& A, const Item& it, int mode) {
   if (threadIdx.x == 0) {
@@ -1646,10 +1648,9 @@ __global__ __launch_bounds__(kThreads, 2) void apq_tile_kernel(KArgs A) {
       continue;
     }
     if (streamable<MODE>(A, it)) {
-      // the ring loads as many activation rows as the item has tokens (1, 2, else 4)
+      // the ring loads as many activation rows as the item has tokens (1 or 2)
       if (it.n <= 1) stream_q<MODE, 1>(A, Qu, i, it, ok, total, sh_tiles, tiles);
-      else if (it.n == 2) stream_q<MODE, 2>(A, Qu, i, it, ok, total, sh_tiles, tiles);
-      else stream_q<MODE, 4>(A, Qu, i, it, ok, total, sh_tiles, tiles);
+      else stream_q<MODE, 2>(A, Qu, i, it, ok, total, sh_tiles, tiles);
     } else {
       switch (it.q) {
         case 1: run_item<MODE, 1>(A, it, Qu); break;

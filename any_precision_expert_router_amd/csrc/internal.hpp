@@ -188,10 +188,19 @@ int check_layer_args(const float* logits, const uint16_t* x, int T, int E, int H
 int launch_apq_gemv(const moe_apq_block& blk, const uint16_t* x, int T, float* y,
                     int dense_threshold, hipStream_t stream);
 
-// Tiles with at least this many tokens use the matrix-core (MFMA) path by default.
+// The product path of a tile of n tokens on a block of width q.  The packed-dot VALU path
+// (streaming) takes at most 2 tokens on blocks of width <= 4, whose 2q-bit pair tables make its
+// decode about half as costly as the matrix-core path's single-entry tables, and single tokens on
+// wider blocks, where both paths decode alike and the matrix cores do the products for free;
+// everything else takes the matrix-core (MFMA) path.  A caller's threshold (the n at or above
+// which a tile must use the MFMA path) can only lower that switch.
 constexpr int kDefaultDenseThreshold = 5;
 inline int effective_dense_threshold(int prefill_threshold) {
   return prefill_threshold > 0 ? prefill_threshold : kDefaultDenseThreshold;
+}
+__host__ __device__ inline int stream_max_tokens(int q) { return q <= 4 ? 2 : 1; }
+__host__ __device__ inline bool takes_stream(int n, int q, int dense_threshold) {
+  return n <= stream_max_tokens(q) && n < dense_threshold;
 }
 int launch_decode_indices(const moe_apq_block& blk, uint8_t* idx_out, hipStream_t stream);
 int launch_routing_stats(const int32_t* offsets, const int32_t* pairs, const float* gates, int E,

@@ -90,7 +90,7 @@ struct GroupSmem {
   int32_t offsets[MOE_MAX_EXPERTS + 1];  // LDS copies of the grouping results for the records
   int32_t active[MOE_MAX_EXPERTS];
   int32_t qslot[2][4][18];                // records: per module, class and order bucket, counts then positions
-  int32_t cls_tot[4];                     // records: per class
+  int32_t cls_tot[2][4];                  // records: per module and class
   int32_t n_active;
 };
 
@@ -308,56 +308,58 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
   const int n_act = sm.n_active;
   const bool split = static_cast<long>(r.T) * r.k <= kRecSplitMaxPairs;
   int e = -1, base = 0, n = 0, groups = 0;
-  bool streaming = false;
-  if (tid < n_act) {
+  // Per module, the records come in four classes: the matrix-core items, then the streaming
+  // items by token count, larger first (3-4, 2, 1; with the current switch at most 2 tokens
+  // stream) -- a streaming workgroup keeps its ring across consecutive
+  // items whose token count fits the ring's, so equal counts are kept together.  Whether an
+  // item streams depends on its block's width (takes_stream), so the two modules of one expert
+  // may fall in different classes; the split into token groups does not (an expert with more
+  // than kRecGroupTok tokens never streams).
+  ExpertRecord rec;
+  int cls[2] = {0, 0}, qm[2] = {0, 0};
+  const bool act_ = tid < n_act;
+  if (act_) {
     e = sm.active[tid];
     base = sm.offsets[e];
     n = sm.offsets[e + 1] - base;
-    streaming = n <= kRecTok && n < r.dense_threshold;
-    groups = !streaming && split && n > kRecGroupTok ? (n + kRecGroupTok - 1) / kRecGroupTok : 1;
+    groups = split && n > kRecGroupTok ? (n + kRecGroupTok - 1) / kRecGroupTok : 1;
+    fill_record(rec, r.table[2 * e], r.table[2 * e + 1], r.I, r);
+    const bool ok = record_ok(rec.meta);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      qm[m] = ok ? record_q(rec.meta, m) : 0;
+      cls[m] = !(ok && takes_stream(n, qm[m], r.dense_threshold)) ? 0 : (n >= 3 ? 1 : (n == 2 ? 2 : 3));
+    }
   }
-  // record totals of the four classes: the multi-token experts, then the streaming experts by
-  // token count (3-4, 2, 1) -- a streaming workgroup keeps its ring across consecutive items
-  // whose token count fits the ring's, so equal counts are kept together
-  const bool act_ = tid < n_act;
   for (int i = tid; i < 2 * 4 * 18; i += blockDim.x) (&sm.qslot[0][0][0])[i] = 0;
-  if (tid < 4) sm.cls_tot[tid] = 0;
-  const int v0[4] = {act_ && !streaming ? groups : 0, act_ && streaming && n >= 3 ? 1 : 0,
-                     act_ && streaming && n == 2 ? 1 : 0, act_ && streaming && n == 1 ? 1 : 0};
+  if (tid < 8) (&sm.cls_tot[0][0])[tid] = 0;
   __syncthreads();  // the grouping's last reads of its LDS are done; the counters are zero
   if (act_) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (v0[c]) atomicAdd(&sm.cls_tot[c], v0[c]);
+    for (int m = 0; m < 2; ++m) atomicAdd(&sm.cls_tot[m][cls[m]], groups);
   }
   __syncthreads();
-  int tot[4];
+  int first[2] = {0, 0};  // per module: records of the classes before this expert's
+  int tot = 0;            // records in all (the same for both modules)
 #pragma unroll
-  for (int c = 0; c < 4; ++c) tot[c] = sm.cls_tot[c];
-  int cls = 0;
+  for (int c = 0; c < 4; ++c) {
+    tot += sm.cls_tot[0][c];
 #pragma unroll
-  for (int c = 1; c < 4; ++c)
-    if (v0[c]) cls = c;
-  int first = 0;  // records of the classes before this expert's
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    if (c < cls) first += tot[c];
+    for (int m = 0; m < 2; ++m)
+      if (c < cls[m]) first[m] += sm.cls_tot[m][c];
+  }
   // Per module, each class's records are ordered roughly by cost, costliest first, so that the
   // queue hands out the longest items first and the tail once it runs dry is shorter: the
   // matrix-core records with wide passes (more than 32 tokens) first, then by that module's
   // width, widest first.  Consecutive streaming items then also share a width more often (their
   // ring continues only across items of one width).  Positions inside a bucket come from LDS
   // atomics: the order only schedules work, every item's result is the same.
-  ExpertRecord rec;
   int bk[2] = {0, 0};
-  if (tid < n_act) {
-    fill_record(rec, r.table[2 * e], r.table[2 * e + 1], r.I, r);
-    const bool ok = record_ok(rec.meta);
-    const bool wide = cls == 0 && n > kRecDensePassTok;
+  if (act_) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      bk[m] = (ok ? record_q(rec.meta, m) : 0) + (wide ? 9 : 0);
-      atomicAdd(&sm.qslot[m][cls][bk[m]], groups);
+      bk[m] = qm[m] + (cls[m] == 0 && n > kRecDensePassTok ? 9 : 0);
+      atomicAdd(&sm.qslot[m][cls[m]][bk[m]], groups);
     }
   }
   __syncthreads();
@@ -374,7 +376,7 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
   if (tid < n_act) {
     int pos_m[2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) pos_m[m] = first + atomicAdd(&sm.qslot[m][cls][bk[m]], groups);
+    for (int m = 0; m < 2; ++m) pos_m[m] = first[m] + atomicAdd(&sm.qslot[m][cls[m]][bk[m]], groups);
     const size_t stride = max_records(r.T, r.E, r.k);
     rec.expert = e;
     for (int g = 0; g < groups; ++g) {
@@ -392,7 +394,7 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
     }
   }
   if (tid == 0) {
-    r.n_recs[0] = tot[0] + tot[1] + tot[2] + tot[3];
+    r.n_recs[0] = tot;
     rec = ExpertRecord{};
     if (r.shared) {
       fill_record(rec, r.shared[0], r.shared[1], r.I_shared, r);

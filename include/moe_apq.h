@@ -143,11 +143,13 @@ int moe_group_by_expert(const int32_t* topk_ids, int T, int k, int E, int32_t* e
  *   shared       device moe_apq_block [2] (gate_up [2*I_shared x H], down [H x I_shared]) or
  *                NULL (then I_shared is ignored); shared_scale fp32 [T] or NULL (= 1).
  *   prefill_threshold: the token count n_e at or above which an expert's tiles (and the shared
- *                expert's, with n = T) use the matrix-core (MFMA) product path instead of the
- *                packed-dot VALU path; <= 0 selects the library default, 5.  The VALU path
- *                holds at most 4 tokens per pass, so values above 5 act as 5: an expert with 5
- *                or more tokens always takes the MFMA path.  Results agree up to fp32
- *                summation order.
+ *                expert's, with n = T) must use the matrix-core (MFMA) product path instead of
+ *                the packed-dot VALU path; <= 0 selects no lowering.  By default a tile streams
+ *                through the VALU path only when n_e <= 2 on a block of width q <= 4 or n_e = 1
+ *                on a wider block (the VALU path's pair tables make q <= 4 cheap to decode), so
+ *                a threshold can only lower that switch: 1 sends every tile to the MFMA path, 2
+ *                streams single tokens only, and values above 2 change nothing.  Results agree
+ *                up to fp32 summation order.
  *   y            out fp16 [T][H].
  *   workspace    >= moe_workspace_bytes(T, E, H, I, k, I_shared) bytes, 256-byte aligned.
  *   Device checks: a routed block whose descriptor does not match (rows, cols) of its module, has
@@ -212,8 +214,9 @@ int moe_apq_pack(const uint8_t* idx8_host, int rows, int cols, int q, uint32_t* 
  *   lookups moe_apq_ffn uses, in its plain mode).
  *   blk_host  host pointer to the descriptor (planes/lut are device pointers, 16-byte aligned).
  *   x         fp16 [T][cols];  y out fp32 [T][rows].
- *   dense_threshold: the tile takes the matrix-core path when T >= min(dense_threshold, 5)
- *             (<= 0: default 5), so that both product paths can be checked on the same block.
+ *   dense_threshold: the tile streams through the VALU path when T < dense_threshold (<= 0: no
+ *             limit) and T <= 2 (q <= 4) or T = 1 (q >= 5), else takes the matrix-core path,
+ *             so that both product paths can be checked on the same block.
  */
 int moe_apq_gemv(const moe_apq_block* blk_host, const uint16_t* x, int T, float* y,
                  int dense_threshold, void* stream);

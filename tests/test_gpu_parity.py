@@ -230,9 +230,10 @@ def test_gemv_one_hot_probe_is_exact_lut_read(q, dense, C):
     y = torch.empty((len(cols), R), dtype=torch.float32, device=DEV)
     if dense == 1:
         apq.moe_apq_gemv(blk, _t(x), y, dense_threshold=1)
-    else:  # the VALU path takes at most 4 tokens per tile
-        for t0 in range(0, len(cols), 4):
-            apq.moe_apq_gemv(blk, _t(x[t0:t0 + 4]), y[t0:t0 + 4], dense_threshold=dense)
+    else:  # the VALU path takes at most 2 tokens per tile at q <= 4, 1 above
+        step = 2 if q <= 4 else 1
+        for t0 in range(0, len(cols), step):
+            apq.moe_apq_gemv(blk, _t(x[t0:t0 + step]), y[t0:t0 + step], dense_threshold=dense)
     idx = oracle.committed_index(idx8, q)
     expect = np.stack([lut[np.arange(R), idx[:, c]].astype(np.float32) for c in cols])
     np.testing.assert_array_equal(y.cpu().numpy(), expect)
@@ -896,13 +897,16 @@ def test_lynx_remapped_layer_matches_oracle():
     assert err <= LAYER_TOL
 
 
-@pytest.mark.parametrize("threshold", [0, 3], ids=["auto", "mfma-from-3"])
+@pytest.mark.parametrize("threshold", [0, 2], ids=["auto", "mfma-from-2"])
 def test_streaming_token_counts_and_ring_switches(threshold):
     """Routing built so that experts 0-3 get 1 token, 4-7 get 2, 8-11 get 3 and 12-15 get 4 (top-2
-    over 20 tokens), at every width 1..8: the streaming ring loads 1, 2 or 4 activation rows by
-    token count, the record step orders the streaming experts by count, and a stream ends where
-    the next item's count does not fit its ring.  With the matrix-core switch at 3 tokens the 3-
-    and 4-token experts take the MFMA branch instead.  Output against the oracle."""
+    over 20 tokens), at every width 1..8 (the two modules of an expert at different widths): the
+    1-token items stream at every width, the 2-token items at widths <= 4 (the ring loads 1 or 2
+    activation rows by token count) and take the matrix-core branch above, the 3- and 4-token
+    items take the matrix-core branch; the record step orders each module's streaming items by
+    count, so the two modules of one expert can sit in different classes, and a stream ends where
+    the next item's width or count does not fit its ring.  With the switch at 2 tokens only the
+    single tokens stream.  Output against the oracle."""
     E, k = 16, 2
     mult = [1] * 4 + [2] * 4 + [3] * 4 + [4] * 4
     slots = [e for e in range(E) for _ in range(mult[e])]          # 40 (token, slot) pairs
