@@ -28,7 +28,6 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
-sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 import workloads as wl  # noqa: E402
 
@@ -124,7 +123,7 @@ def cpu_threads() -> int:
 def cpu_baseline(shape, inputs, budget_s: float, threads: int):
     """The float64 oracle on the host cores: one whole layer call (all tokens), median of runs."""
     import oracle
-    import gpu_layers
+    from workloads import device as gpu_layers
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
@@ -162,7 +161,7 @@ def layer_copies(apq, torch, shape, dev, copies_gb):
     """The layer's device blocks and page table, plus clones at other addresses (same bytes) so
     that the rotated copies exceed the last-level cache.  Shapes that differ only in their token
     count share one set of weights."""
-    import gpu_layers
+    from workloads import device as gpu_layers
     key = (shape.workload_id, shape.E, shape.H, shape.I, shape.I_shared)
     if key in _copies_cache:
         return _copies_cache[key]
@@ -215,7 +214,7 @@ class LayerCall:
 def check_parity(call, tokens):
     """Layer output of one call against the float64 oracle: relative L2 over the checked tokens
     (all of them, or a list), and the worst single token."""
-    import gpu_layers
+    from workloads import device as gpu_layers
     import oracle
     shape = call.shape
     call.step(0)
@@ -285,7 +284,7 @@ def rooflines(call, ids, kernel_us, workload):
 
 def sub_record(apq, torch, name, dev, args):
     """One other layer shape: parity, then the eager time per layer and the kernel rooflines."""
-    import gpu_layers
+    from workloads import device as gpu_layers
     import oracle
     shape = WORKLOADS[name]
     log(f"[bench] sub-record {name}: building weights")
@@ -317,7 +316,7 @@ def prefill_row(apq, torch, dev, steps: int, warmup: int, check: bool, copies_gb
     layer, where about 256 tokens meet every expert and the tile kernels take their wide
     matrix-core branch.  Compute-bound: reported as TFLOP/s of the layer's algorithmic flops
     2*T*k*3*H*I against the fp16 MFMA peak."""
-    import gpu_layers
+    from workloads import device as gpu_layers
     import oracle
     shape = WORKLOADS["qwen2_57b_a14b_prefill2048"]
     log(f"[bench] prefill row: {shape.name}, T={shape.T}")
@@ -440,7 +439,7 @@ def next_rows(apq, torch, call, base, dev, n):
     residency-aware substitution, LYNX remapping, width planning and commits.  The
     single-workgroup kernels are timed as `n` back-to-back launches between two events (inputs
     prepared beforehand, one copy per launch where a launch rewrites its input)."""
-    import gpu_layers
+    from workloads import device as gpu_layers
     import oracle
     shape, stream = call.shape, call.stream
     T, E, k = shape.T, shape.E, shape.k
@@ -560,7 +559,7 @@ def main():
 
     import torch
     import any_precision_expert_router_amd as apq
-    import gpu_layers
+    from workloads import device as gpu_layers
     import oracle
 
     dev = "cuda:0"

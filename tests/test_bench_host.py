@@ -12,7 +12,7 @@ import oracle
 import workloads as wl
 
 sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__))))
-import gpu_layers  # noqa: E402
+from workloads import device as gpu_layers  # noqa: E402
 
 SHAPES = [wl.QWEN15_MOE_A27B, wl.MIXTRAL_8X7B, wl.QWEN3_NEXT_80B_A3B, wl.QWEN2_57B_A14B.with_tokens(8)]
 

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 import any_precision_expert_router_amd as apq  # noqa: E402
-import gpu_layers  # noqa: E402
+from workloads import device as gpu_layers  # noqa: E402
 
 DEV = "cuda"
 

@@ -1,6 +1,7 @@
-"""Glue for the GPU tests and the benchmark: seeded layer inputs -> device-resident blocks and
-page table (through the library's host packer), and oracle block getters for the same blocks.
-Imports the oracle only to build its block getter; the device path never calls it."""
+"""The seeded synthetic layers on the device, for the GPU tests, smoke() and the benchmark: blocks
+packed by the library's host packer and uploaded with their page table (device_layer), the same
+blocks in the (indices, width, LUT) form the oracle takes (oracle_getters: plain data, the oracle
+itself is not imported here), and the weight bytes one call reads (active_weight_bytes)."""
 from __future__ import annotations
 
 import functools
