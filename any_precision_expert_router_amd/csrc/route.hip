@@ -25,12 +25,6 @@ namespace {
 
 constexpr int kRouteWaves = 4;  // tokens per 256-thread workgroup
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 // One wavefront routes token t: each lane holds PER_LANE candidate keys; k rounds of the
 // wavefront maximum select the experts in order; the gates are the softmax of the k logits.
 template <int PER_LANE>
@@ -55,7 +49,9 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     if (lane == j) mine = win;
   }
   const float l0 = key_value(readlane64(mine, 0));
-  const float z = lane < k ? expf(key_value(mine) - l0) : 0.0f;
+  // computed on every lane and selected, so that no branch (EXEC write) precedes the DPP sum
+  const float ez = expf(key_value(mine) - l0);
+  const float z = lane < k ? ez : 0.0f;
   const float s = wave_sum_f32(z);
   if (lane < k) {
     const int32_t id = key_id(mine);
@@ -116,13 +112,11 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
   __syncthreads();
 
   // exclusive scans of count[e] and of (count[e] > 0), one thread per expert (E <= 1024)
-  const int c = tid < E ? sm.count[tid] : 0;
-  int a = c, f = c > 0 ? 1 : 0;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int a2 = __shfl_up(a, off, 64), f2 = __shfl_up(f, off, 64);
-    if (lane >= off) { a += a2; f += f2; }
-  }
+  // count[] has room for every thread: loaded on every lane and selected, so that no branch
+  // (EXEC write) precedes the DPP scans
+  const int cnt = sm.count[tid];
+  const int c = tid < E ? cnt : 0;
+  const int a = wave_inclusive_add(c), f = wave_inclusive_add(c > 0 ? 1 : 0);
   if (lane == 63) { sm.wave_tot[0][wave] = a; sm.wave_tot[1][wave] = f; }
   __syncthreads();
   int base_a = 0, base_f = 0;

@@ -62,6 +62,29 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return ab > cd ? ab : cd;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront by DPP: shifts by 1, 2, 4 and 8 inside
+// each 16-lane row (lanes without a source add 0), then the total of row 0 broadcast into row 1
+// and of row 2 into row 3, then the total of rows 0-1 into rows 2-3.  Every lane must be active.
+__device__ __forceinline__ int wave_inclusive_add(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Wavefront sum of an fp32 value, returned uniform: DPP butterflies inside each 16-lane row, then
+// the four row sums through scalar registers, in the fixed order (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false));
+  return (lane_float(v, 0) + lane_float(v, 16)) + (lane_float(v, 32) + lane_float(v, 48));
+}
+
 // Wavefront maximum of a 64-bit key, returned uniform: the maximum high word, then the maximum
 // low word among the lanes that hold it (the lexicographic order of the two words is the order of
 // the key), as two 32-bit reductions.  Every lane of the wavefront must be active.
