@@ -72,6 +72,14 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_topk_kernel(
   route_token<PER_LANE>(logits + static_cast<size_t>(t) * E, E, k, ids + o, gates + o, nullptr, nullptr);
 }
 
+// Workgroup barrier for LDS traffic only (see lds_barrier); the routing kernels' global stores
+// (ids, gates, offsets, pairs, records) stay in flight across it.
+__device__ __forceinline__ void group_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" : : : "memory");
+}
+
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupMapBytes = 16384;  // LDS of the stable placement (slot map or segment counters)
 
@@ -103,13 +111,13 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
   const int TK = T * k;
 
   for (int e = tid; e < E; e += kGroupThreads) sm.count[e] = 0;
-  __syncthreads();
+  group_barrier();
   // an id outside [0, E) names no expert: its pair is not placed (offsets[E] counts placed pairs)
   for (int p = tid; p < TK; p += kGroupThreads) {
     const int e = ids[p];
     if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&sm.count[e], 1);
   }
-  __syncthreads();
+  group_barrier();
 
   // exclusive scans of count[e] and of (count[e] > 0), one thread per expert (E <= 1024)
   // count[] has room for every thread: loaded on every lane and selected, so that no branch
@@ -118,7 +126,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
   const int c = tid < E ? cnt : 0;
   const int a = wave_inclusive_add(c), f = wave_inclusive_add(c > 0 ? 1 : 0);
   if (lane == 63) { sm.wave_tot[0][wave] = a; sm.wave_tot[1][wave] = f; }
-  __syncthreads();
+  group_barrier();
   int base_a = 0, base_f = 0;
   for (int w = 0; w < wave; ++w) { base_a += sm.wave_tot[0][w]; base_f += sm.wave_tot[1][w]; }
   const int excl = base_a + a - c;
@@ -137,7 +145,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
     n_active[0] = act_pos + (c > 0 ? 1 : 0);
     sm.n_active = act_pos + (c > 0 ? 1 : 0);
   }
-  __syncthreads();
+  group_barrier();
   // -1 padding after the active list
   int n_act = 0;
   for (int w = 0; w < kGroupThreads / 64; ++w) n_act += sm.wave_tot[1][w];
@@ -158,7 +166,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
       sm.seg_pos[i] = 0;
       if constexpr (!DISTINCT) sm.dup_tag[i] = -1;
     }
-    __syncthreads();
+    group_barrier();
     const int t_begin = min(T, wave * seg_len), t_end = min(T, t_begin + seg_len);
     if (wave < S) {
       for (int i = t_begin * k + lane; i < t_end * k; i += 64) {
@@ -166,7 +174,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
         if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&sm.seg_pos[wave * E + e], 1);
       }
     }
-    __syncthreads();
+    group_barrier();
     if (tid < E) {
       int run = excl;
       for (int w = 0; w < S; ++w) {
@@ -175,7 +183,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
         run += n;
       }
     }
-    __syncthreads();
+    group_barrier();
     if (wave < S && lane < k) {
       constexpr int kBatch = 16;  // expert ids loaded ahead of the in-order placement
       int32_t* pos_of = sm.seg_pos + wave * E;
@@ -237,7 +245,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
         }
       }
     }
-    __syncthreads();
+    group_barrier();
   } else {
     // stable placement, chunk by chunk over tokens: because the k experts of one token are
     // distinct, a pair's rank inside its expert is the number of earlier tokens that picked it
@@ -246,12 +254,12 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
     for (int t0 = 0; t0 < T; t0 += chunk) {
       const int tn = min(chunk, T - t0);
       for (int i = tid; i < tn * E; i += kGroupThreads) sm.slot_map[i] = 0;
-      __syncthreads();
+      group_barrier();
       for (int i = tid; i < tn * k; i += kGroupThreads) {
         const int tt = i / k, j = i - tt * k;
         sm.slot_map[tt * E + ids[(t0 + tt) * k + j]] = static_cast<uint8_t>(j + 1);
       }
-      __syncthreads();
+      group_barrier();
       if (tid < E && c > 0) {
         for (int tt = 0; tt < tn; ++tt) {
           const int s = sm.slot_map[tt * E + tid];
@@ -262,7 +270,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
           }
         }
       }
-      __syncthreads();
+      group_barrier();
     }
   }
 }
@@ -274,10 +282,11 @@ __global__ __launch_bounds__(kGroupThreads) void group_by_expert_kernel(
   group_body<true>(ids, T, k, E, offsets, pairs, active, n_active, sm, nullptr);
 }
 
+// The tests are combined without short-circuit, so that no field's load waits on another's test.
 __device__ __forceinline__ bool block_valid(const moe_apq_block& b, int rows, int cols) {
   const uintptr_t align = reinterpret_cast<uintptr_t>(b.planes) | reinterpret_cast<uintptr_t>(b.lut);
-  return b.planes != nullptr && b.lut != nullptr && (align & 15) == 0 && b.rows == rows &&
-         b.cols == cols && b.q >= 1 && b.q <= 8 && b.state == MOE_PAGE_GPU;
+  return (b.planes != nullptr) & (b.lut != nullptr) & ((align & 15) == 0) & (b.rows == rows) &
+         (b.cols == cols) & (b.q >= 1) & (b.q <= 8) & (b.state == MOE_PAGE_GPU);
 }
 
 __device__ __forceinline__ void fill_record(ExpertRecord& rec, const moe_apq_block& gu,
@@ -286,7 +295,7 @@ __device__ __forceinline__ void fill_record(ExpertRecord& rec, const moe_apq_blo
   rec.planes[1] = dn.planes;
   rec.lut[0] = gu.lut;
   rec.lut[1] = dn.lut;
-  rec.meta = record_meta(gu.q, dn.q, block_valid(gu, 2 * inter, r.H) && block_valid(dn, r.H, inter));
+  rec.meta = record_meta(gu.q, dn.q, block_valid(gu, 2 * inter, r.H) & block_valid(dn, r.H, inter));
 }
 
 // Records of the shared expert and of the routed experts, the count of routed records, and
@@ -327,12 +336,12 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
   }
   for (int i = tid; i < 2 * 4 * 18; i += blockDim.x) (&sm.qslot[0][0][0])[i] = 0;
   if (tid < 8) (&sm.cls_tot[0][0])[tid] = 0;
-  __syncthreads();  // the grouping's last reads of its LDS are done; the counters are zero
+  group_barrier();  // the grouping's last reads of its LDS are done; the counters are zero
   if (act_) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) atomicAdd(&sm.cls_tot[m][cls[m]], groups);
   }
-  __syncthreads();
+  group_barrier();
   int first[2] = {0, 0};  // per module: records of the classes before this expert's
   int tot = 0;            // records in all (the same for both modules)
 #pragma unroll
@@ -356,7 +365,7 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
       atomicAdd(&sm.qslot[m][cls[m]][bk[m]], groups);
     }
   }
-  __syncthreads();
+  group_barrier();
   if (tid < 8) {
     const int m = tid >> 2, c = tid & 3;
     int run = 0;
@@ -366,7 +375,7 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
       run += cnt;
     }
   }
-  __syncthreads();
+  group_barrier();
   if (tid < n_act) {
     int pos_m[2];
 #pragma unroll
@@ -428,9 +437,9 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_records_kernel(
     route_token<PER_LANE>(logits + static_cast<size_t>(t) * E, E, k, ids + o, gates + o, s_ids + o,
                           s_gates + o);
   }
-  __syncthreads();
+  group_barrier();
   group_body<false>(s_ids, T, k, E, offsets, pairs, active, n_active, sm, s_pairs);
-  __syncthreads();
+  group_barrier();
   records_body(sm, s_pairs, s_gates, r);
 }
 
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kGroupThreads) void group_records_kernel(
   __shared__ GroupSmem sm;
   // the ids come from route_topk: every token names k distinct experts
   group_body<true, true>(ids, r.T, r.k, r.E, offsets, pairs, active, n_active, sm, nullptr);
-  __syncthreads();
+  __syncthreads();  // records_body reads the pairs stored above from global memory
   records_body(sm, pairs, r.gates, r);
 }
 
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(kGroupThreads) void records_kernel(
   for (int e = threadIdx.x; e <= r.E; e += blockDim.x) sm.offsets[e] = offsets[e];
   for (int e = threadIdx.x; e < r.E; e += blockDim.x) sm.active[e] = active[e];
   if (threadIdx.x == 0) sm.n_active = n_active[0];
-  __syncthreads();
+  group_barrier();
   records_body(sm, pairs, r.gates, r);
 }
 
