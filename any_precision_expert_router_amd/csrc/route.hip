@@ -295,7 +295,9 @@ __device__ __forceinline__ void fill_record(ExpertRecord& rec, const moe_apq_blo
   rec.planes[1] = dn.planes;
   rec.lut[0] = gu.lut;
   rec.lut[1] = dn.lut;
-  rec.meta = record_meta(gu.q, dn.q, block_valid(gu, 2 * inter, r.H) & block_valid(dn, r.H, inter));
+  const int ok = static_cast<int>(block_valid(gu, 2 * inter, r.H)) &
+                 static_cast<int>(block_valid(dn, r.H, inter));
+  rec.meta = record_meta(gu.q, dn.q, ok != 0);
 }
 
 // Records of the shared expert and of the routed experts, the count of routed records, and
