@@ -9,12 +9,13 @@
 // the k selected logits.
 //
 // Grouping (LYNX, 1 Problem statement: decode loads each distinct expert the batch activates):
-// one workgroup.  Counts per expert by LDS integer atomics (order-free, so deterministic), an
-// exclusive scan for the CSR offsets and the ascending active-expert list, then a stable
-// placement (pair id ascending inside an expert).  Routing output names k distinct experts per
-// token, so a pair's rank inside its expert is the number of earlier pairs that picked that
-// expert: small batches walk an LDS token x expert slot map with one thread per expert, large
-// batches run a segmented counting sort (one wavefront per run of tokens).  The standalone
+// one workgroup.  Per-expert counts, an exclusive scan for the CSR offsets and the ascending
+// active-expert list, then a stable placement (pair id ascending inside an expert).  Routing
+// output names k distinct experts per token, so a pair's rank inside its expert is the number of
+// earlier pairs that picked that expert: small batches fill an LDS token x expert slot map and
+// one thread per expert counts and then walks its column; large batches run a segmented
+// counting sort (one wavefront per run of tokens, per-segment counts by LDS integer atomics,
+// which are order-free and so deterministic).  The standalone
 // grouping also accepts ids it did not produce: an id outside [0, E) is not placed, and a token
 // that names an expert twice is placed in slot order.
 #include "internal.hpp"
@@ -84,10 +85,9 @@ constexpr int kGroupThreads = 1024;
 constexpr int kGroupMapBytes = 16384;  // LDS of the stable placement (slot map or segment counters)
 
 struct GroupSmem {
-  int32_t count[MOE_MAX_EXPERTS];
-  int32_t wave_tot[4][kGroupThreads / 64];
+  int32_t wave_tot[2][kGroupThreads / 64];  // per wavefront: pairs, active experts
   union {
-    uint8_t slot_map[kGroupMapBytes];     // small batches: token x expert slot map per chunk
+    uint8_t slot_map[kGroupMapBytes];     // small batches: token x expert slot map
     int32_t seg_pos[kGroupMapBytes / 4];  // large batches: [segments][E] pair counts, then positions
   };
   int32_t dup_tag[kGroupMapBytes / 4];    // large batches: [segments][E] last token that named e
@@ -97,38 +97,40 @@ struct GroupSmem {
   int32_t cls_tot[2][4];                  // records: per module and class
   int32_t n_active;
 };
+static_assert(kFusedRouteMaxT * MOE_MAX_EXPERTS <= kGroupMapBytes, "a fused call's slot map fits");
 
-// Stable grouping by one workgroup of kGroupThreads threads.  `ids` may have been written by this
-// workgroup before a barrier.  SEGMENTED picks the placement: a segmented counting sort (large
-// batches: every wavefront places its own run of tokens), or a token x expert slot map walked by
-// one thread per expert (small batches, where it measured faster).
-template <bool SEGMENTED, bool DISTINCT = false>
-__device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
-                           int32_t* __restrict__ pairs, int32_t* __restrict__ active,
-                           int32_t* __restrict__ n_active, GroupSmem& sm, int32_t* pairs_lds) {
+// The records' counters start at zero; cleared with the grouping's own LDS, before its first
+// barrier.
+__device__ __forceinline__ void zero_record_counters(GroupSmem& sm) {
+  const int tid = threadIdx.x;
+  if (tid < 2 * 4 * 18) (&sm.qslot[0][0][0])[tid] = 0;
+  if (tid < 8) (&sm.cls_tot[0][0])[tid] = 0;
+}
+
+// Exclusive scans of the per-expert pair counts and of (count > 0), one thread per expert
+// (thread e holds c = count of expert e, 0 for e >= E), then the CSR offsets, the ascending
+// active-expert list (-1 after it) and their LDS copies.  Returns the expert's first position.
+// One barrier (the wavefront totals).
+__device__ __forceinline__ int scan_counts(int c, int E, int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                           GroupSmem& sm) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int TK = T * k;
-
-  for (int e = tid; e < E; e += kGroupThreads) sm.count[e] = 0;
-  group_barrier();
-  // an id outside [0, E) names no expert: its pair is not placed (offsets[E] counts placed pairs)
-  for (int p = tid; p < TK; p += kGroupThreads) {
-    const int e = ids[p];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&sm.count[e], 1);
+  const int a = wave_inclusive_add(c), f = wave_inclusive_add(c > 0 ? 1 : 0);
+  if (lane == 63) {
+    sm.wave_tot[0][wave] = a;
+    sm.wave_tot[1][wave] = f;
   }
   group_barrier();
-
-  // exclusive scans of count[e] and of (count[e] > 0), one thread per expert (E <= 1024)
-  // count[] has room for every thread: loaded on every lane and selected, so that no branch
-  // (EXEC write) precedes the DPP scans
-  const int cnt = sm.count[tid];
-  const int c = tid < E ? cnt : 0;
-  const int a = wave_inclusive_add(c), f = wave_inclusive_add(c > 0 ? 1 : 0);
-  if (lane == 63) { sm.wave_tot[0][wave] = a; sm.wave_tot[1][wave] = f; }
-  group_barrier();
-  int base_a = 0, base_f = 0;
-  for (int w = 0; w < wave; ++w) { base_a += sm.wave_tot[0][w]; base_f += sm.wave_tot[1][w]; }
+  int base_a = 0, base_f = 0, n_act = 0;
+  for (int w = 0; w < kGroupThreads / 64; ++w) {
+    const int ta = sm.wave_tot[0][w], tf = sm.wave_tot[1][w];
+    if (w < wave) {
+      base_a += ta;
+      base_f += tf;
+    }
+    n_act += tf;
+  }
   const int excl = base_a + a - c;
   const int act_pos = base_f + f - (c > 0 ? 1 : 0);
   if (tid < E) {
@@ -138,19 +140,37 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
       active[act_pos] = tid;
       sm.active[act_pos] = tid;
     }
+    if (tid >= n_act) active[tid] = -1;
   }
   if (tid == E - 1) {
     offsets[E] = excl + c;
     sm.offsets[E] = excl + c;
-    n_active[0] = act_pos + (c > 0 ? 1 : 0);
-    sm.n_active = act_pos + (c > 0 ? 1 : 0);
   }
-  group_barrier();
-  // -1 padding after the active list
-  int n_act = 0;
-  for (int w = 0; w < kGroupThreads / 64; ++w) n_act += sm.wave_tot[1][w];
-  for (int e = tid; e < E; e += kGroupThreads)
-    if (e >= n_act) active[e] = -1;
+  if (tid == 0) {
+    n_active[0] = n_act;
+    sm.n_active = n_act;
+  }
+  return excl;
+}
+
+// Stable grouping by one workgroup of kGroupThreads threads (E <= kGroupThreads).  `ids` may
+// have been written by this workgroup before a barrier.  SEGMENTED picks the placement: a
+// segmented counting sort (large batches: every wavefront places its own run of tokens), or a
+// token x expert slot map walked by one thread per expert (small batches, T * E <=
+// kGroupMapBytes, where it measured faster).  Each placement counts the pairs per expert from
+// its own map, so the grouping takes four barriers (slot map) or five (segmented).  The caller
+// places the barrier after it (the results are in global memory and in LDS: offsets, active,
+// n_active, pairs and pairs_lds); it also clears the records' counters.
+template <bool SEGMENTED, bool DISTINCT = false>
+__device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
+                           int32_t* __restrict__ pairs, int32_t* __restrict__ active,
+                           int32_t* __restrict__ n_active, GroupSmem& sm, int32_t* pairs_lds) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  // this thread's expert for the per-expert loops; threads past E read expert 0's column and
+  // drop it (a select, so that no branch (EXEC write) precedes the DPP scans)
+  const int e_ld = tid < E ? tid : 0;
+  zero_record_counters(sm);
 
   if constexpr (SEGMENTED) {
     // stable placement by a segmented counting sort: the tokens are cut into S consecutive
@@ -159,7 +179,8 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
     // first position, and each wavefront then walks its tokens in order, lane j placing slot j.
     // When a token's k experts are distinct (always so for routing output), its k lanes never
     // update the same position counter; a token that names an expert twice takes an exact,
-    // slower path that keeps the slot order.
+    // slower path that keeps the slot order.  An id outside [0, E) names no expert: its pair is
+    // not placed (offsets[E] counts placed pairs).
     const int S = max(1, min(kGroupThreads / 64, static_cast<int>(kGroupMapBytes / (4 * E))));
     const int seg_len = (T + S - 1) / S;
     for (int i = tid; i < S * E; i += kGroupThreads) {
@@ -175,6 +196,10 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
       }
     }
     group_barrier();
+    int cnt = 0;
+    for (int w = 0; w < S; ++w) cnt += sm.seg_pos[w * E + e_ld];
+    const int c = tid < E ? cnt : 0;
+    const int excl = scan_counts(c, E, offsets, active, n_active, sm);
     if (tid < E) {
       int run = excl;
       for (int w = 0; w < S; ++w) {
@@ -219,7 +244,7 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
             } else {
               // repeated experts: the first slot naming an expert takes positions for all of
               // them, each slot its rank among them (slot order, so the sort stays stable)
-              int rank = 0, cnt = 0, first = lane;
+              int rank = 0, cnt2 = 0, first = lane;
               for (int j2 = 0; j2 < k; ++j2) {
                 const int e2 = __shfl(eu, j2, 64);
                 if (e2 == eu) {
@@ -227,13 +252,13 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
                     ++rank;
                     first = min(first, j2);
                   }
-                  ++cnt;
+                  ++cnt2;
                 }
               }
               int base = 0;
               if (valid && rank == 0) {
                 base = pos_of[eu];
-                pos_of[eu] = base + cnt;
+                pos_of[eu] = base + cnt2;
               }
               base = __shfl(base, first, 64);
               if (valid) {
@@ -245,32 +270,34 @@ __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int
         }
       }
     }
-    group_barrier();
   } else {
-    // stable placement, chunk by chunk over tokens: because the k experts of one token are
-    // distinct, a pair's rank inside its expert is the number of earlier tokens that picked it
-    int cursor = excl;
-    const int chunk = kGroupMapBytes / E > 0 ? kGroupMapBytes / E : 1;
-    for (int t0 = 0; t0 < T; t0 += chunk) {
-      const int tn = min(chunk, T - t0);
-      for (int i = tid; i < tn * E; i += kGroupThreads) sm.slot_map[i] = 0;
-      group_barrier();
-      for (int i = tid; i < tn * k; i += kGroupThreads) {
-        const int tt = i / k, j = i - tt * k;
-        sm.slot_map[tt * E + ids[(t0 + tt) * k + j]] = static_cast<uint8_t>(j + 1);
-      }
-      group_barrier();
-      if (tid < E && c > 0) {
-        for (int tt = 0; tt < tn; ++tt) {
-          const int s = sm.slot_map[tt * E + tid];
-          if (s) {
-            const int p = (t0 + tt) * k + (s - 1);
-            if (pairs_lds) pairs_lds[cursor] = p;
-            pairs[cursor++] = p;
-          }
+    // stable placement through a token x expert slot map (the whole call in one map): because
+    // the k experts of one token are distinct, a pair's rank inside its expert is the number of
+    // earlier tokens that picked it.  Thread e counts its column, then walks it again in token
+    // order from its offset.
+    uint32_t* map32 = reinterpret_cast<uint32_t*>(sm.slot_map);
+    for (int i = tid; 4 * i < T * E; i += kGroupThreads) map32[i] = 0u;
+    group_barrier();
+    for (int i = tid; i < T * k; i += kGroupThreads) {
+      const int tt = i / k, j = i - tt * k;
+      const int e = ids[i];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E))
+        sm.slot_map[tt * E + e] = static_cast<uint8_t>(j + 1);
+    }
+    group_barrier();
+    int cnt = 0;
+    for (int tt = 0; tt < T; ++tt) cnt += sm.slot_map[tt * E + e_ld] != 0 ? 1 : 0;
+    const int c = tid < E ? cnt : 0;
+    int cursor = scan_counts(c, E, offsets, active, n_active, sm);
+    if (tid < E && c > 0) {
+      for (int tt = 0; tt < T; ++tt) {
+        const int sl = sm.slot_map[tt * E + tid];
+        if (sl) {
+          const int p = tt * k + (sl - 1);
+          if (pairs_lds) pairs_lds[cursor] = p;
+          pairs[cursor++] = p;
         }
       }
-      group_barrier();
     }
   }
 }
@@ -304,12 +331,11 @@ __device__ __forceinline__ void fill_record(ExpertRecord& rec, const moe_apq_blo
 // zeroed work counters.  One thread per active expert (blockDim >= E).  Multi-token experts'
 // records come first, split into token groups in small calls, then the streaming experts'
 // (split and order: see kRecGroupTok in internal.hpp).  The grouping comes from this workgroup's
-// LDS copies (after a barrier); pairs and gates from LDS when the routing ran in this workgroup,
-// else from global memory.
+// LDS copies (after a barrier, with the order counters cleared before it: zero_record_counters);
+// pairs and gates from LDS when the routing ran in this workgroup, else from global memory.
 __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* gates,
                              const RecordArgs& r) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const int n_act = sm.n_active;
   const bool split = static_cast<long>(r.T) * r.k <= kRecSplitMaxPairs;
   int e = -1, base = 0, n = 0, groups = 0;
@@ -336,12 +362,32 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
       cls[m] = !(ok && takes_stream(n, qm[m], r.dense_threshold)) ? 0 : (n >= 3 ? 1 : (n == 2 ? 2 : 3));
     }
   }
-  for (int i = tid; i < 2 * 4 * 18; i += blockDim.x) (&sm.qslot[0][0][0])[i] = 0;
-  if (tid < 8) (&sm.cls_tot[0][0])[tid] = 0;
-  group_barrier();  // the grouping's last reads of its LDS are done; the counters are zero
+  // Per module, each class's records are ordered roughly by cost, costliest first, so that the
+  // queue hands out the longest items first and the tail once it runs dry is shorter: the
+  // matrix-core records with wide passes (more than 32 tokens) first, then by that module's
+  // width, widest first.  Consecutive streaming items then also share a width more often (their
+  // ring continues only across items of one width).  Positions inside a bucket come from LDS
+  // atomics: the order only schedules work, every item's result is the same.  The counters
+  // were cleared before the grouping's first barrier.
+  int bk[2] = {0, 0};
   if (act_) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) atomicAdd(&sm.cls_tot[m][cls[m]], groups);
+    for (int m = 0; m < 2; ++m) {
+      bk[m] = qm[m] + (cls[m] == 0 && n > kRecDensePassTok ? 9 : 0);
+      atomicAdd(&sm.qslot[m][cls[m]][bk[m]], groups);
+    }
+  }
+  group_barrier();
+  // per module and class: bucket counts -> first positions inside the class, and its total
+  if (tid < 8) {
+    const int m = tid >> 2, c = tid & 3;
+    int run = 0;
+    for (int b = 17; b >= 0; --b) {
+      const int cnt = sm.qslot[m][c][b];
+      sm.qslot[m][c][b] = run;
+      run += cnt;
+    }
+    sm.cls_tot[m][c] = run;
   }
   group_barrier();
   int first[2] = {0, 0};  // per module: records of the classes before this expert's
@@ -353,31 +399,6 @@ __device__ void records_body(GroupSmem& sm, const int32_t* pairs, const float* g
     for (int m = 0; m < 2; ++m)
       if (c < cls[m]) first[m] += sm.cls_tot[m][c];
   }
-  // Per module, each class's records are ordered roughly by cost, costliest first, so that the
-  // queue hands out the longest items first and the tail once it runs dry is shorter: the
-  // matrix-core records with wide passes (more than 32 tokens) first, then by that module's
-  // width, widest first.  Consecutive streaming items then also share a width more often (their
-  // ring continues only across items of one width).  Positions inside a bucket come from LDS
-  // atomics: the order only schedules work, every item's result is the same.
-  int bk[2] = {0, 0};
-  if (act_) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      bk[m] = qm[m] + (cls[m] == 0 && n > kRecDensePassTok ? 9 : 0);
-      atomicAdd(&sm.qslot[m][cls[m]][bk[m]], groups);
-    }
-  }
-  group_barrier();
-  if (tid < 8) {
-    const int m = tid >> 2, c = tid & 3;
-    int run = 0;
-    for (int b = 17; b >= 0; --b) {
-      const int cnt = sm.qslot[m][c][b];
-      sm.qslot[m][c][b] = run;
-      run += cnt;
-    }
-  }
-  group_barrier();
   if (tid < n_act) {
     int pos_m[2];
 #pragma unroll
@@ -462,6 +483,7 @@ __global__ __launch_bounds__(kGroupThreads) void records_kernel(
   for (int e = threadIdx.x; e <= r.E; e += blockDim.x) sm.offsets[e] = offsets[e];
   for (int e = threadIdx.x; e < r.E; e += blockDim.x) sm.active[e] = active[e];
   if (threadIdx.x == 0) sm.n_active = n_active[0];
+  zero_record_counters(sm);
   group_barrier();
   records_body(sm, pairs, r.gates, r);
 }
