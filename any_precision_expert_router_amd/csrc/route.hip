@@ -158,9 +158,9 @@ __device__ __forceinline__ int scan_counts(int c, int E, int32_t* __restrict__ o
 // segmented counting sort (large batches: every wavefront places its own run of tokens), or a
 // token x expert slot map walked by one thread per expert (small batches, T * E <=
 // kGroupMapBytes, where it measured faster).  Each placement counts the pairs per expert from
-// its own map, so the grouping takes four barriers (slot map) or five (segmented).  The caller
-// places the barrier after it (the results are in global memory and in LDS: offsets, active,
-// n_active, pairs and pairs_lds); it also clears the records' counters.
+// its own map, so the grouping takes three barriers (slot map) or four (segmented), plus the one
+// the caller places after it before anything reads the results (offsets, active, n_active,
+// pairs and pairs_lds, in global memory and in LDS).  It also clears the records' counters.
 template <bool SEGMENTED, bool DISTINCT = false>
 __device__ __forceinline__ void group_body(const int32_t* ids, int T, int k, int E, int32_t* __restrict__ offsets,
                            int32_t* __restrict__ pairs, int32_t* __restrict__ active,
