@@ -393,15 +393,17 @@ _ws_layers = {}
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (4, 60, 4), (11, 512, 10), (13, 1024, 32), (16, 60, 4),
-                                   (16, 1024, 32), (16, 8, 8), (17, 60, 4), (64, 512, 10), (2048, 64, 8)])
+                                   (16, 1024, 32), (16, 8, 8), (17, 60, 4), (64, 512, 10), (2048, 64, 8),
+                                   (1, 1, 1), (9, 128, 1), (5, 3, 3), (16, 2, 2), (40, 1, 1)])
 @pytest.mark.parametrize("ties", [False, True], ids=["matmul", "ties"])
 def test_layer_workspace_routing_bit_exact(T, E, k, ties):
     """The routing and grouping a moe_layer_forward call computes and leaves in its workspace --
     top-k ids, gates, expert offsets and sorted pairs -- against the oracle, bit for bit (gates
     within 1e-6).  Calls of at most 16 tokens run routing, grouping and the expert records in one
     fused single-workgroup kernel (token x expert slot map); larger ones use the separate routing
-    and segmented grouping kernels.  Shapes cover both paths, E from 8 to 1024 and k up to 32;
-    "ties" rounds the logits to the fp16 grid and plants equal and signed-zero logits."""
+    and segmented grouping kernels.  Shapes cover both paths, E from 1 to 1024, k from 1 to 32
+    and k = E (every expert active); "ties" rounds the logits to the fp16 grid and plants equal
+    and signed-zero logits."""
     say(f"layer workspace routing T={T} E={E} k={k} ties={ties}")
     shape = wl.TINY.replace(H=128, E=E, I=128, k=k, T=T, name="workspace routing")
     if E not in _ws_layers:
